@@ -1,0 +1,153 @@
+/*
+ * pasa_attn.h -- C ABI of the PASA forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  "Online Pseudo-average Shifting Attention (PASA) for Robust
+ * Low-precision LLM Inference", Abstract: PASA computes attention
+ *     O = softmax(scale * Q K^T) V
+ * blockwise, Flash-Attention style, with the score tiles, the exponentials and
+ * the running softmax statistics held in half precision.  Each key block's
+ * scores are shifted by a per-row pseudo-average (online pseudo-average
+ * shifting) so the half-precision tile stays below the fp16 maximum 65504, and
+ * an epilogue (global recovering) re-applies the removed shifts so the softmax
+ * normalisation and the log-sum-exp are exact up to rounding.  The result is
+ * mathematically equivalent to plain softmax attention.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are DEVICE pointers (HIP global memory) unless stated otherwise.
+ *    The caller owns every buffer.  The library allocates nothing, never
+ *    synchronises, keeps no global state and is safe to call from several host
+ *    threads on different streams.
+ *  - Work is enqueued on `stream` (0 = the null stream) and runs asynchronously;
+ *    the return code reports argument validation and launch errors only.
+ *  - Element types: q, k, v, o are IEEE binary16 (fp16); lse is fp32.
+ *  - Layout: contiguous BSHD.  q, o are [batch, seqlen_q, num_heads_q, head_dim];
+ *    k, v are [batch, seqlen_kv, num_heads_q / gqa_group, head_dim];
+ *    lse is [batch, num_heads_q, seqlen_q].  Query head h reads key/value head
+ *    h / gqa_group.
+ *  - lse holds ln(sum_j exp(softmax_scale * q_i . k_j)) over the visible keys,
+ *    natural logarithm; a row with no visible key gets o = 0 and lse = -inf.
+ *  - Causal masking is aligned to the bottom-right corner: key j is visible to
+ *    query i iff j <= i + seqlen_kv - seqlen_q.
+ *  - On any error nothing is enqueued and no output byte is written.
+ *  - Supported: head_dim 64 or 128; num_heads_q % gqa_group == 0; any
+ *    batch >= 1 and sequence lengths >= 1 (ragged tails are masked).
+ *    seqlen_kv <= 65504 for pasa_attn_fwd and pasa_naive_attn_fwd, because the
+ *    running softmax sum is carried in fp16; the split-KV decode path has no
+ *    such bound (each split's sum is at most 65504 keys; the combine is fp32).
+ */
+#ifndef PASA_ATTN_H
+#define PASA_ATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PASA_OK = 0,
+    PASA_ERR_INVALID = -1,     /* null pointer, non-positive size, bad GQA group */
+    PASA_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels implement */
+    PASA_ERR_WORKSPACE = -3,   /* decode workspace missing or too small */
+    PASA_ERR_HIP = -4          /* the HIP runtime reported a launch error */
+} pasa_status;
+
+/*
+ * PASA prefill / full forward pass ("Online Pseudo-average Shifting Attention
+ * (PASA) ...", Abstract: online pseudo-average shifting, half-precision
+ * softmax, global recovering).
+ *   q, k, v   device, fp16, layouts above.       o   device, fp16, written.
+ *   lse       device fp32 [B,Hq,Sq], written; may be NULL (not computed).
+ *   softmax_scale  multiplies q.k before the softmax (e.g. 1/sqrt(head_dim)).
+ *   causal    0 or 1 (bottom-right aligned).
+ * Errors: PASA_ERR_INVALID for a null q/k/v/o, a size < 1, or
+ * num_heads_q % gqa_group != 0; PASA_ERR_UNSUPPORTED for head_dim not in
+ * {64,128}, seqlen_kv > 65504, a non-finite or non-positive softmax_scale, or
+ * sizes whose element count overflows 64-bit indexing.
+ */
+int pasa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group,
+                  int head_dim, float softmax_scale, int causal, hipStream_t stream);
+
+/*
+ * Naive fp16 Flash-Attention forward: the same blockwise kernel WITHOUT the
+ * pseudo-average shift.  The unscaled score tile QK^T is rounded to fp16 and
+ * then multiplied by the scale in fp16, as a plain half-precision Flash
+ * Attention would; scores above 65504 become +-inf and the output turns to
+ * inf/NaN.  It exists to exhibit the overflow the PASA page describes
+ * ("Online Pseudo-average Shifting Attention (PASA) ...", Abstract: overflow
+ * above 65504 caused by a large sequence-dimension bias and by query/key
+ * resonance).  Arguments, layouts and errors as pasa_attn_fwd.
+ */
+int pasa_naive_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int batch, int seqlen_q, int seqlen_kv, int num_heads_q,
+                        int gqa_group, int head_dim, float softmax_scale, int causal,
+                        hipStream_t stream);
+
+/*
+ * Split-KV decode: one query token per sequence against a KV cache.
+ * The keys [0, seqlen_kv) are cut into num_splits contiguous ranges; each range
+ * yields a normalised partial (o_s, lse_s) computed with the PASA tile numerics,
+ * and a combine step merges them.  Partials over disjoint key ranges compose
+ * exactly once each is re-weighted by its own log-sum-exp ("Block Sparse Flash
+ * Attention" topic page, FoldAttention card: softmax is invariant to a common
+ * shift; additive partials compose split KV).
+ *   q        device fp16 [batch, 1, num_heads_q, head_dim]
+ *   k_cache, v_cache  device fp16 [batch, seqlen_kv, num_heads_q/gqa_group, head_dim]
+ *   o        device fp16 [batch, 1, num_heads_q, head_dim], written
+ *   lse      device fp32 [batch, num_heads_q], written; may be NULL
+ *   num_splits  >= 1, or 0 to let the library choose (pasa_attn_decode_splits).
+ *   workspace   device memory of at least
+ *               pasa_attn_decode_workspace_bytes(batch, num_heads_q, head_dim, n)
+ *               bytes (n = the split count actually used), 256-byte aligned.
+ *               It holds the fp32 partials: o_part [batch, num_heads_q, n, head_dim]
+ *               followed, at the next 256-byte boundary, by
+ *               lse_part [batch, num_heads_q, n].  Its contents on return are
+ *               the partials of this call.
+ * Launches the split kernel and the combine kernel on `stream`, in order.
+ * Errors: as pasa_attn_fwd (without the seqlen_kv bound), plus
+ * PASA_ERR_WORKSPACE for a null, misaligned or too-small workspace, and
+ * PASA_ERR_INVALID for num_splits < 0.  More splits than key blocks are
+ * clamped to the number of 64-key blocks.
+ */
+int pasa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
+                     float* lse, int batch, int seqlen_kv, int num_heads_q, int gqa_group,
+                     int head_dim, float softmax_scale, int num_splits, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/* The split count pasa_attn_decode uses for num_splits = 0 (host function, no
+ * device work): enough (sequence, key/value head, split) work items to fill the
+ * chip, clamped to the number of 64-key blocks.  Returns 0 on invalid sizes. */
+int pasa_attn_decode_splits(int batch, int seqlen_kv, int num_heads_q, int gqa_group);
+
+/* Workspace size in bytes for pasa_attn_decode with num_splits splits (host
+ * function).  Returns 0 on invalid sizes. */
+size_t pasa_attn_decode_workspace_bytes(int batch, int num_heads_q, int head_dim,
+                                        int num_splits);
+
+/*
+ * Combine step alone (global recovering across splits):
+ *   M = max_s lse_s,  lse = M + ln sum_s exp(lse_s - M),
+ *   o = sum_s exp(lse_s - lse) * o_s      (fp32 arithmetic, o rounded to fp16).
+ * Partials with lse_s = -inf carry no weight; if every partial is empty the
+ * row gets o = 0 and lse = -inf.
+ *   o_part    device fp32 [batch, num_heads_q, num_splits, head_dim]
+ *   lse_part  device fp32 [batch, num_heads_q, num_splits]
+ *   o         device fp16 [batch, 1, num_heads_q, head_dim], written
+ *   lse       device fp32 [batch, num_heads_q], written; may be NULL
+ * Errors: PASA_ERR_INVALID for null o_part/lse_part/o or sizes < 1;
+ * PASA_ERR_UNSUPPORTED for head_dim not in {64,128}.
+ */
+int pasa_attn_decode_combine(const float* o_part, const float* lse_part, void* o,
+                             float* lse, int batch, int num_heads_q, int head_dim,
+                             int num_splits, hipStream_t stream);
+
+/* Human-readable text for a pasa_status value (static storage). */
+const char* pasa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PASA_ATTN_H */

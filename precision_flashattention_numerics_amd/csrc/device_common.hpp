@@ -1,0 +1,61 @@
+// Device-side helpers shared by the PASA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pasa {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D(32x32, fp32) += A(32x16, fp16) * B(16x32, fp16) on the matrix cores.
+// Lane l supplies A row (l % 32), B column (l % 32), and 8 consecutive
+// contraction slots starting at 8 * (l / 32); it receives D column (l % 32),
+// rows 8 * (r / 4) + 4 * (l / 32) + (r % 4) for r = 0..15.
+__device__ __forceinline__ f16v mfma_32x32x16(h8 a, h8 b, f16v c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Exchange with the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float xor32(float x) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(((int)__lane_id() ^ 32) << 2,
+                                                       __float_as_int(x)));
+}
+__device__ __forceinline__ _Float16 xor32(_Float16 x) {
+    unsigned short u = __builtin_bit_cast(unsigned short, x);
+    int r = __builtin_amdgcn_ds_bpermute(((int)__lane_id() ^ 32) << 2, (int)u);
+    return __builtin_bit_cast(_Float16, (unsigned short)r);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) {
+    return __builtin_amdgcn_ballot_w64(p) != 0;
+}
+
+__device__ __forceinline__ _Float16 hexp2(_Float16 x) { return __builtin_elementwise_exp2(x); }
+
+__device__ __forceinline__ h2 hexp2(h2 x) {
+    h2 r;
+    r.x = __builtin_elementwise_exp2(x.x);
+    r.y = __builtin_elementwise_exp2(x.y);
+    return r;
+}
+
+__device__ __forceinline__ h2 hmax(h2 a, h2 b) { return __builtin_elementwise_max(a, b); }
+
+// Two floats rounded to fp16 (round-to-nearest-even) and packed.
+__device__ __forceinline__ h2 to_h2(float a, float b) {
+    return __builtin_convertvector((float __attribute__((ext_vector_type(2)))){a, b}, h2);
+}
+
+constexpr _Float16 kHalfNegInf = -__builtin_inff16();
+
+}  // namespace pasa

@@ -1,0 +1,40 @@
+// Host-side launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace pasa {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int batch, seqlen_q, seqlen_kv, num_heads_q, gqa_group, head_dim;
+    float softmax_scale;
+    int causal;
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    float* o_part;     // [batch, num_heads_q, num_splits, head_dim]
+    float* lse_part;   // [batch, num_heads_q, num_splits]
+    int batch, seqlen_kv, num_heads_q, gqa_group, head_dim;
+    float softmax_scale;
+    int num_splits;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, bool naive, hipStream_t stream);
+hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_combine(const float* o_part, const float* lse_part, void* o, float* lse,
+                                 int batch, int num_heads_q, int head_dim, int num_splits,
+                                 hipStream_t stream);
+
+// Keys per split-kernel workgroup iteration; splits are whole multiples of it.
+constexpr int kDecodeBlock = 128;
+
+}  // namespace pasa

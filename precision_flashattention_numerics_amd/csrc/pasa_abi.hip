@@ -1,0 +1,149 @@
+// C ABI of the PASA library: argument validation and dispatch to the kernels.
+// The declarations, with the passages each operation follows, are in
+// include/pasa_attn.h.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/pasa_attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kMaxFp16Sum = 65504;   // fp16 running sum: at most this many keys
+
+bool supported_dim(int d) { return d == 64 || d == 128; }
+
+// Element counts must stay below 2^62 so 64-bit indexing cannot overflow.
+bool fits(int64_t a, int64_t b, int64_t c, int64_t d) {
+    const double p = (double)a * (double)b * (double)c * (double)d;
+    return p < 4.0e18;
+}
+
+int check_common(const void* q, const void* k, const void* v, const void* o, int batch,
+                 int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group, int head_dim,
+                 float softmax_scale) {
+    if (!q || !k || !v || !o) return PASA_ERR_INVALID;
+    if (batch < 1 || seqlen_q < 1 || seqlen_kv < 1 || num_heads_q < 1 || gqa_group < 1 ||
+        head_dim < 1)
+        return PASA_ERR_INVALID;
+    if (num_heads_q % gqa_group != 0) return PASA_ERR_INVALID;
+    if (!supported_dim(head_dim)) return PASA_ERR_UNSUPPORTED;
+    if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return PASA_ERR_UNSUPPORTED;
+    if (!fits(batch, seqlen_q, num_heads_q, head_dim) ||
+        !fits(batch, seqlen_kv, num_heads_q, head_dim))
+        return PASA_ERR_UNSUPPORTED;
+    if (seqlen_q > 65535 * 128) return PASA_ERR_UNSUPPORTED;   // grid y limit
+    if (batch > 65535) return PASA_ERR_UNSUPPORTED;            // grid z limit
+    return PASA_OK;
+}
+
+int fwd_common(bool naive, const void* q, const void* k, const void* v, void* o, float* lse,
+               int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group,
+               int head_dim, float softmax_scale, int causal, hipStream_t stream) {
+    int rc = check_common(q, k, v, o, batch, seqlen_q, seqlen_kv, num_heads_q, gqa_group,
+                          head_dim, softmax_scale);
+    if (rc != PASA_OK) return rc;
+    if (causal != 0 && causal != 1) return PASA_ERR_INVALID;
+    if (seqlen_kv > kMaxFp16Sum) return PASA_ERR_UNSUPPORTED;
+    pasa::FwdArgs a{q, k, v, o, lse, batch, seqlen_q, seqlen_kv, num_heads_q, gqa_group,
+                    head_dim, softmax_scale, causal};
+    return pasa::launch_fwd(a, naive, stream) == hipSuccess ? PASA_OK : PASA_ERR_HIP;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+int pasa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                  int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group, int head_dim,
+                  float softmax_scale, int causal, hipStream_t stream) {
+    return fwd_common(false, q, k, v, o, lse, batch, seqlen_q, seqlen_kv, num_heads_q, gqa_group,
+                      head_dim, softmax_scale, causal, stream);
+}
+
+int pasa_naive_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group,
+                        int head_dim, float softmax_scale, int causal, hipStream_t stream) {
+    return fwd_common(true, q, k, v, o, lse, batch, seqlen_q, seqlen_kv, num_heads_q, gqa_group,
+                      head_dim, softmax_scale, causal, stream);
+}
+
+int pasa_attn_decode_splits(int batch, int seqlen_kv, int num_heads_q, int gqa_group) {
+    if (batch < 1 || seqlen_kv < 1 || num_heads_q < 1 || gqa_group < 1 ||
+        num_heads_q % gqa_group != 0)
+        return 0;
+    const int64_t units = (int64_t)batch * (num_heads_q / gqa_group) * ((gqa_group + 31) / 32);
+    const int64_t target = 1024;   // workgroups: four per compute unit on 256 CUs
+    int64_t n = (target + units - 1) / units;
+    const int64_t blocks = (seqlen_kv + pasa::kDecodeBlock - 1) / pasa::kDecodeBlock;
+    if (n > blocks) n = blocks;
+    if (n > 65535) n = 65535;
+    return (int)(n < 1 ? 1 : n);
+}
+
+size_t pasa_attn_decode_workspace_bytes(int batch, int num_heads_q, int head_dim,
+                                        int num_splits) {
+    if (batch < 1 || num_heads_q < 1 || head_dim < 1 || num_splits < 1) return 0;
+    const size_t rows = (size_t)batch * num_heads_q * num_splits;
+    return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+int pasa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
+                     float* lse, int batch, int seqlen_kv, int num_heads_q, int gqa_group,
+                     int head_dim, float softmax_scale, int num_splits, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_common(q, k_cache, v_cache, o, batch, 1, seqlen_kv, num_heads_q, gqa_group,
+                          head_dim, softmax_scale);
+    if (rc != PASA_OK) return rc;
+    if (num_splits < 0) return PASA_ERR_INVALID;
+    int n = num_splits == 0 ? pasa_attn_decode_splits(batch, seqlen_kv, num_heads_q, gqa_group)
+                            : num_splits;
+    const int blocks = (seqlen_kv + pasa::kDecodeBlock - 1) / pasa::kDecodeBlock;
+    if (n > blocks) n = blocks;
+    if (n > 65535) return PASA_ERR_UNSUPPORTED;
+    // every split sums at most 65504 keys in fp16
+    const int per_split = (blocks + n - 1) / n * pasa::kDecodeBlock;
+    if (per_split > kMaxFp16Sum) return PASA_ERR_UNSUPPORTED;
+    const size_t need = pasa_attn_decode_workspace_bytes(batch, num_heads_q, head_dim, n);
+    if (workspace == nullptr || ((uintptr_t)workspace & 255) != 0 || workspace_bytes < need)
+        return PASA_ERR_WORKSPACE;
+    const size_t rows = (size_t)batch * num_heads_q * n;
+    float* o_part = (float*)workspace;
+    float* lse_part = (float*)((char*)workspace + align256(rows * head_dim * sizeof(float)));
+    pasa::DecodeArgs a{q, k_cache, v_cache, o_part, lse_part, batch, seqlen_kv, num_heads_q,
+                       gqa_group, head_dim, softmax_scale, n};
+    if (pasa::launch_decode_split(a, stream) != hipSuccess) return PASA_ERR_HIP;
+    if (pasa::launch_decode_combine(o_part, lse_part, o, lse, batch, num_heads_q, head_dim, n,
+                                    stream) != hipSuccess)
+        return PASA_ERR_HIP;
+    return PASA_OK;
+}
+
+int pasa_attn_decode_combine(const float* o_part, const float* lse_part, void* o, float* lse,
+                             int batch, int num_heads_q, int head_dim, int num_splits,
+                             hipStream_t stream) {
+    if (!o_part || !lse_part || !o) return PASA_ERR_INVALID;
+    if (batch < 1 || num_heads_q < 1 || head_dim < 1 || num_splits < 1) return PASA_ERR_INVALID;
+    if (!supported_dim(head_dim)) return PASA_ERR_UNSUPPORTED;
+    if ((int64_t)batch * num_heads_q > 0x7fffffff) return PASA_ERR_UNSUPPORTED;
+    return pasa::launch_decode_combine(o_part, lse_part, o, lse, batch, num_heads_q, head_dim,
+                                       num_splits, stream) == hipSuccess
+               ? PASA_OK
+               : PASA_ERR_HIP;
+}
+
+const char* pasa_status_string(int status) {
+    switch (status) {
+        case PASA_OK: return "ok";
+        case PASA_ERR_INVALID: return "invalid argument";
+        case PASA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case PASA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case PASA_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

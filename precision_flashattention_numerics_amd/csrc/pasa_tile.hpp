@@ -1,0 +1,287 @@
+// Building blocks shared by the PASA prefill and decode kernels: K/V staging
+// into LDS, and the per-block half-precision softmax with online
+// pseudo-average shifting.
+//
+// Method: "Online Pseudo-average Shifting Attention (PASA) for Robust
+// Low-precision LLM Inference", Abstract (online pseudo-average shifting,
+// half-precision Flash-Attention process, global recovering).  The page gives
+// no equations; the per-row rules below are this library's reading of it:
+//
+//   mu    = mean of the row's visible scores S in the block         (fp32)
+//   off   = c*mu on the row's first visible block, else max(c*mu, R) (fp32)
+//   T     = fp16_rne(c*S - off), masked keys -> -inf                  (fp16)
+//   m_b   = max_j T                                                   (fp16)
+//   if m_b > THETA (the tile's largest entries sit where fp16 is
+//   coarse, or overflowed): off = max_j c*S over visible keys, and T,
+//   m_b are recomputed                                                (rare)
+//   R'    = max(R, off + m_b)      running maximum, log2 units        (fp32)
+//   s     = fp16(R' - off);  P = exp2(T - s);  r = sum_j P            (fp16)
+//   alpha = exp2(fp16(R - R'))                                        (fp16)
+//   (l_hi, l_lo) <- compensated fp16 sum of alpha*(l_hi, l_lo) + r    (fp16)
+// where c = scale * log2(e).  Because T and s are taken relative to the same
+// off, P = exp2(c*S - R') whatever off was: the shift changes only which fp16
+// numbers are formed, never the softmax (a per-row shift leaves softmax
+// unchanged).  The epilogue recovers the exact log-sum-exp as
+// ln2 * (R + log2(l_hi + l_lo)).
+//
+// The naive variant rounds the UNSCALED S to fp16, scales it in fp16 and
+// keeps a plain running maximum: a half-precision Flash Attention without the
+// shift, which overflows when |QK^T| > 65504.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace pasa {
+
+constexpr float kTheta = 4.0f;   // refine threshold on the tile maximum (log2 units)
+
+// Row permutation applied to K when it feeds S^T = K Q^T: swaps bits 2 and 3
+// of the row index, so lane l's 16 scores of a 32-key sub-tile are the keys
+// 16*(r/8) + 8*(l/32) + (r%8): two runs of 8 consecutive keys, which is the
+// B-operand layout of the following P V product.
+__device__ __forceinline__ int sigma(int n) {
+    return (n & ~0xC) | ((n & 4) << 1) | ((n & 8) >> 1);
+}
+
+// Key offset (within a 32-key sub-tile) of accumulator register r of lane
+// half hh (= lane / 32).
+__device__ __forceinline__ int key_of(int r, int hh) {
+    return 16 * (r >> 3) + 8 * hh + (r & 7);
+}
+
+// Compensated fp16 accumulation (hi, lo) <- alpha * (hi, lo) + r: a
+// two-sum in fp16 carries the rounding error of each addition in lo.
+__device__ __forceinline__ void comp_add(_Float16& hi, _Float16& lo, _Float16 alpha, _Float16 r) {
+#pragma clang fp contract(off)
+    _Float16 a = alpha * hi;
+    _Float16 b = alpha * lo;
+    _Float16 s = a + r;
+    _Float16 bb = s - a;
+    _Float16 err = (a - (s - bb)) + (r - bb);
+    hi = s;
+    lo = b + err;
+}
+
+struct RowState {
+    float R = -__builtin_inff();   // running maximum of c*S (log2 units)
+    _Float16 lhi = 0, llo = 0;     // running sum (PASA): compensated fp16 pair
+    float lsum = 0.0f;             // running sum (naive): fp32
+};
+
+// One key block of NT 32-key sub-tiles for the row held by this lane (and by
+// the lane 32 apart, which holds the other half of the row's keys).
+//   S       fp32 scores (unscaled q.k), register r of sub-tile t is key
+//           32*t + key_of(r, hh) of the block
+//   full    every key of the block is visible to every row of the wave
+//   cnt     number of keys of the block visible to this row
+//   vis     vis(t, r) -> visibility of that key (used only when !full)
+// Writes P (packed fp16 pairs, P[8*t + r/2] = keys r, r+1 of sub-tile t) and
+// returns alpha, the factor the caller applies to its accumulator.
+template <int NT, bool NAIVE, typename Vis>
+__device__ __forceinline__ _Float16 softmax_block(const f16v (&S)[NT], h2 (&P)[8 * NT],
+                                                  RowState& st, float c, bool full, int cnt,
+                                                  Vis vis) {
+    h2 T[8 * NT];
+    _Float16 mb;
+    float off = 0.0f;
+    if (!NAIVE) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum += (full || vis(t, r)) ? S[t][r] : 0.0f;
+        sum += xor32(sum);
+        const float cmu = cnt > 0 ? c * (sum / (float)cnt) : st.R;
+        off = (st.R == -__builtin_inff()) ? cmu : fmaxf(cmu, st.R);
+
+        auto make_tile = [&](float o) -> _Float16 {
+            h2 mm = (h2){kHalfNegInf, kHalfNegInf};
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    h2 x = to_h2(__builtin_fmaf(c, S[t][r], -o), __builtin_fmaf(c, S[t][r + 1], -o));
+                    if (!full) {
+                        if (!vis(t, r)) x.x = kHalfNegInf;
+                        if (!vis(t, r + 1)) x.y = kHalfNegInf;
+                    }
+                    T[8 * t + r / 2] = x;
+                    mm = hmax(mm, x);
+                }
+            _Float16 m = mm.x > mm.y ? mm.x : mm.y;
+            _Float16 p = xor32(m);
+            return m > p ? m : p;
+        };
+        mb = make_tile(off);
+        // NaN-safe: an overflowed (+inf) or NaN maximum also triggers it
+        const bool need = cnt > 0 && !(mb <= (_Float16)kTheta);
+        if (wave_any(need)) {
+            float m32 = -__builtin_inff();
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (full || vis(t, r)) m32 = fmaxf(m32, S[t][r]);
+            m32 = fmaxf(m32, xor32(m32));
+            if (need) off = c * m32;
+            mb = make_tile(off);
+        }
+    } else {
+        const _Float16 ch = (_Float16)c;
+        h2 mm = (h2){kHalfNegInf, kHalfNegInf};
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                h2 x = to_h2(S[t][r], S[t][r + 1]) * (h2){ch, ch};
+                if (!full) {
+                    if (!vis(t, r)) x.x = kHalfNegInf;
+                    if (!vis(t, r + 1)) x.y = kHalfNegInf;
+                }
+                T[8 * t + r / 2] = x;
+                mm = hmax(mm, x);
+            }
+        _Float16 m = mm.x > mm.y ? mm.x : mm.y;
+        _Float16 p = xor32(m);
+        mb = m > p ? m : p;
+    }
+
+    const float Rn = cnt > 0 ? fmaxf(st.R, off + (float)mb) : st.R;
+    const _Float16 s = cnt > 0 ? (_Float16)(Rn - off) : (_Float16)0;
+    const h2 s2 = {s, s};
+#pragma unroll
+    for (int i = 0; i < 8 * NT; ++i) P[i] = hexp2(T[i] - s2);
+
+    // fp16 pairwise tree sum of the lane's exponentials, then across halves
+    h2 a[4 * NT];
+#pragma unroll
+    for (int i = 0; i < 4 * NT; ++i) a[i] = P[2 * i] + P[2 * i + 1];
+#pragma unroll
+    for (int w = 2 * NT; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) a[i] = a[2 * i] + a[2 * i + 1];
+    _Float16 rsum = a[0].x + a[0].y;
+    rsum = rsum + xor32(rsum);
+
+    const _Float16 alpha = cnt > 0 ? hexp2((_Float16)(st.R - Rn)) : (_Float16)1;
+    if (!NAIVE)
+        comp_add(st.lhi, st.llo, alpha, rsum);
+    else
+        st.lsum = (float)alpha * st.lsum + (float)rsum;
+    st.R = Rn;
+    return alpha;
+}
+
+template <bool NAIVE>
+__device__ __forceinline__ float row_sum(const RowState& st) {
+    return NAIVE ? st.lsum : (float)st.lhi + (float)st.llo;
+}
+
+// Cooperative staging of one block of BKEYS keys x D head-dim columns:
+// K kept row-major (row stride KPAD halves), V transposed (V^T, row stride
+// VPAD halves) so that the P V product reads 8 consecutive keys per lane.
+template <int D, int BKEYS, int THREADS>
+struct Stager {
+    static constexpr int KPAD = D + 8;        // 16-byte pad: conflict-free 16 B reads
+    static constexpr int VPAD = BKEYS + 8;
+    static constexpr int K_HALVES = BKEYS * KPAD;
+    static constexpr int V_HALVES = D * VPAD;
+    static constexpr int STAGE_HALVES = K_HALVES + V_HALVES;
+    static constexpr int KCH = (BKEYS * D / 8 + THREADS - 1) / THREADS;  // 16 B K chunks per thread
+    static constexpr int VUNITS = (BKEYS / 4) * (D / 8);                 // 4 keys x 8 columns
+    static constexpr int VCH = (VUNITS + THREADS - 1) / THREADS;
+
+    h8 kreg[KCH];
+    h8 vreg[VCH][4];
+
+    __device__ __forceinline__ void load(const _Float16* kb, const _Float16* vb,
+                                         int64_t stride, int base, int nkeys, int tid) {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int chunk = tid + THREADS * i;
+            const int row = chunk / (D / 8), col = chunk % (D / 8);
+            const int key = base + row;
+            kreg[i] = (chunk < BKEYS * D / 8 && key < nkeys)
+                          ? *(const h8*)(kb + (int64_t)key * stride + 8 * col)
+                          : (h8){};
+        }
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+            const int u = tid + THREADS * i;
+            const int kg = u % (BKEYS / 4), dg = u / (BKEYS / 4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = base + 4 * kg + r;
+                vreg[i][r] = (u < VUNITS && key < nkeys)
+                                 ? *(const h8*)(vb + (int64_t)key * stride + 8 * dg)
+                                 : (h8){};
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(_Float16* Ks, int tid) const {
+        _Float16* Vt = Ks + K_HALVES;
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int chunk = tid + THREADS * i;
+            if (chunk < BKEYS * D / 8) {
+                const int row = chunk / (D / 8), col = chunk % (D / 8);
+                *(h8*)(Ks + row * KPAD + 8 * col) = kreg[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+            const int u = tid + THREADS * i;
+            if (u < VUNITS) {
+                const int kg = u % (BKEYS / 4), dg = u / (BKEYS / 4);
+                // 4 keys x 8 columns -> 8 columns x 4 keys, with byte permutes:
+                // word j of a row holds columns 2j (low half) and 2j+1 (high).
+                u4 r0 = __builtin_bit_cast(u4, vreg[i][0]);
+                u4 r1 = __builtin_bit_cast(u4, vreg[i][1]);
+                u4 r2 = __builtin_bit_cast(u4, vreg[i][2]);
+                u4 r3 = __builtin_bit_cast(u4, vreg[i][3]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const u2 lo = {__builtin_amdgcn_perm(r1[j], r0[j], 0x05040100u),
+                                   __builtin_amdgcn_perm(r3[j], r2[j], 0x05040100u)};
+                    const u2 hi = {__builtin_amdgcn_perm(r1[j], r0[j], 0x07060302u),
+                                   __builtin_amdgcn_perm(r3[j], r2[j], 0x07060302u)};
+                    *(u2*)(Vt + (8 * dg + 2 * j) * VPAD + 4 * kg) = lo;
+                    *(u2*)(Vt + (8 * dg + 2 * j + 1) * VPAD + 4 * kg) = hi;
+                }
+            }
+        }
+    }
+};
+
+// S^T (32 keys x 32 query columns) for the keys at rows [row0, row0+32) of
+// the staged K tile; qreg is the B operand (query column l%32, 8 columns of
+// the head dimension per 16-wide contraction step).
+template <int D, int KPAD>
+__device__ __forceinline__ f16v qk_subtile(const _Float16* Ks, int row0, const h8 (&qreg)[D / 16],
+                                           int n, int hh) {
+    f16v s = (f16v){};
+    const _Float16* krow = Ks + (row0 + sigma(n)) * KPAD + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) s = mfma_32x32x16(*(const h8*)(krow + 16 * kk), qreg[kk], s);
+    return s;
+}
+
+// O^T += V^T P^T for the 16-key chunks [16*ch0, 16*ch0 + 16*NCH) of the
+// staged V^T tile, with P from softmax_block (packed pairs).
+template <int D, int VPAD, int NCH>
+__device__ __forceinline__ void pv_chunks(const _Float16* Vt, int ch0, const h2* P,
+                                          f16v (&acc)[D / 32], int n, int hh) {
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        const h2 p0 = P[4 * ch + 0], p1 = P[4 * ch + 1], p2 = P[4 * ch + 2], p3 = P[4 * ch + 3];
+        const h8 bp = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const h8 a = *(const h8*)(Vt + (32 * dt + n) * VPAD + 16 * (ch0 + ch) + 8 * hh);
+            acc[dt] = mfma_32x32x16(a, bp, acc[dt]);
+        }
+    }
+}
+
+}  // namespace pasa

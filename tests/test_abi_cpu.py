@@ -1,0 +1,102 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/pasa_attn.h declares, and rejects invalid arguments
+with the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pasa_attn.h")
+LIB = os.path.join(ROOT, "precision_flashattention_numerics_amd", "libpasa_attn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pasa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch  # noqa: F401  share torch's HIP runtime, as the binding does
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    for fn in ("pasa_attn_fwd", "pasa_naive_attn_fwd", "pasa_attn_decode",
+               "pasa_attn_decode_combine", "pasa_attn_decode_workspace_bytes",
+               "pasa_attn_decode_splits", "pasa_status_string"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for fn in declared():
+        assert hasattr(lib, fn), fn
+
+
+P = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def _fwd(lib, name, q=P, k=P, v=P, o=P, B=1, Sq=8, Skv=8, Hq=2, g=1, D=64, scale=0.125, causal=0):
+    f = getattr(lib, name)
+    f.restype = ctypes.c_int
+    return f(q, k, v, o, None, B, Sq, Skv, Hq, g, D, ctypes.c_float(scale), causal, None)
+
+
+@pytest.mark.parametrize("name", ["pasa_attn_fwd", "pasa_naive_attn_fwd"])
+def test_fwd_validation(lib, name):
+    assert _fwd(lib, name, q=None) == -1
+    assert _fwd(lib, name, o=None) == -1
+    assert _fwd(lib, name, B=0) == -1
+    assert _fwd(lib, name, Sq=0) == -1
+    assert _fwd(lib, name, Skv=-3) == -1
+    assert _fwd(lib, name, Hq=7, g=2) == -1
+    assert _fwd(lib, name, causal=2) == -1
+    assert _fwd(lib, name, D=96) == -2
+    assert _fwd(lib, name, D=256) == -2
+    assert _fwd(lib, name, Skv=65505) == -2
+    assert _fwd(lib, name, scale=0.0) == -2
+    assert _fwd(lib, name, scale=float("nan")) == -2
+
+
+def test_decode_validation_and_sizes(lib):
+    lib.pasa_attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.pasa_attn_decode.restype = ctypes.c_int
+    ws = lib.pasa_attn_decode_workspace_bytes(64, 28, 128, 4)
+    rows = 64 * 28 * 4
+    assert ws == ((rows * 128 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+    assert lib.pasa_attn_decode_workspace_bytes(0, 28, 128, 4) == 0
+    assert lib.pasa_attn_decode_splits(64, 8192, 28, 7) >= 1
+    assert lib.pasa_attn_decode_splits(1, 100, 1, 1) == 1      # one 128-key block
+    assert lib.pasa_attn_decode_splits(1, 8192, 28, 3) == 0    # 28 % 3 != 0
+
+    def dec(ws_ptr=P, ws_bytes=1 << 30, D=128, n=4, g=7, q=P):
+        return lib.pasa_attn_decode(q, P, P, P, None, 64, 8192, 28, g, D, ctypes.c_float(0.08),
+                                    n, ws_ptr, ctypes.c_size_t(ws_bytes), None)
+    assert dec(q=None) == -1
+    assert dec(g=3) == -1
+    assert dec(n=-1) == -1
+    assert dec(D=80) == -2
+    assert dec(ws_ptr=None) == -3
+    assert dec(ws_ptr=ctypes.c_void_p(0x1010)) == -3            # not 256-byte aligned
+    assert dec(ws_bytes=ws - 1) == -3
+
+
+def test_combine_validation(lib):
+    f = lib.pasa_attn_decode_combine
+    f.restype = ctypes.c_int
+    assert f(None, P, P, None, 1, 1, 128, 2, None) == -1
+    assert f(P, P, P, None, 1, 1, 128, 0, None) == -1
+    assert f(P, P, P, None, 1, 1, 48, 2, None) == -2
+
+
+def test_status_strings(lib):
+    lib.pasa_status_string.restype = ctypes.c_char_p
+    texts = {lib.pasa_status_string(s) for s in (0, -1, -2, -3, -4)}
+    assert len(texts) == 5
+    assert lib.pasa_status_string(17) == b"unknown status"

@@ -1,0 +1,216 @@
+"""GPU parity: the HIP path against the binary64 oracle on identical seeded
+fp16 inputs.  The bar is relative RMSE of O <= 2e-3 and no inf/NaN; lse within
+1e-2 absolute (or 1e-6 relative above 1e4).  The naive fp16 kernel's overflow
+on the large-bias and resonance inputs is recorded alongside."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attn_fp64, combine_fp64
+from tests.gpu_common import (REL_RMSE_MAX, gather_rows, lse_error, lse_ok, nonfinite, rel_rmse,
+                              sample_rows, say, to_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pasa():
+    import precision_flashattention_numerics_amd as p
+    return p
+
+
+def run_fwd(pasa, w, naive=False):
+    import torch
+    q, k, v = W.generate(w)
+    tq, tk, tv = to_gpu(q, k, v)
+    fn = pasa.naive_attn_fwd if naive else pasa.attn_fwd
+    o, lse = fn(tq, tk, tv, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    return (q, k, v), o.cpu().numpy(), lse.cpu().numpy()
+
+
+SMALL = [(B, Sq, Skv, Hq, Hkv, D, causal)
+         for (B, Sq, Skv) in [(1, 1, 1), (1, 63, 63), (2, 64, 64), (1, 65, 65), (1, 127, 300),
+                              (1, 300, 127), (1, 300, 300), (2, 129, 1000)]
+         for (Hq, Hkv) in [(1, 1), (7, 1)]
+         for D in (64, 128)
+         for causal in (False, True)]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_small_shapes_vs_oracle(pasa, shape):
+    B, Sq, Skv, Hq, Hkv, D, causal = shape
+    w = W.custom(B, Sq, Skv, Hq, Hkv, D, causal, kind="bias", seed=sum(shape), bias=3.0)
+    say("case", shape)
+    (q, k, v), o, lse = run_fwd(pasa, w)
+    ro, rl = attn_fp64(q, k, v, w.scale, causal)
+    assert nonfinite(o) == 0
+    # rows with no visible key (causal, Sq > Skv) are exactly zero
+    empty = np.isneginf(rl)
+    if empty.any():
+        b, h, i = np.nonzero(empty)
+        assert np.all(o[b, i, h] == 0)
+    err = rel_rmse(o, ro)
+    say("rel_rmse", err)
+    assert err <= REL_RMSE_MAX
+    assert lse_ok(lse, rl)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_config_full_vs_oracle(pasa, name):
+    w = W.CONFIGS[name]
+    say("config", name)
+    (q, k, v), o, lse = run_fwd(pasa, w)
+    ro, rl = attn_fp64(q, k, v, w.scale, w.causal)
+    n_bad = nonfinite(o) + nonfinite(lse)
+    err = rel_rmse(o, ro)
+    say(name, "rel_rmse", err, "nonfinite", n_bad, "lse_err", lse_error(lse, rl)[:2])
+    assert n_bad == 0
+    assert err <= REL_RMSE_MAX
+    assert lse_ok(lse, rl)
+
+
+def test_c4_sampled_rows_vs_oracle(pasa):
+    w = W.CONFIGS["c4"]
+    say("config c4 (sampled rows)")
+    (q, k, v), o, lse = run_fwd(pasa, w)
+    assert nonfinite(o) == 0 and nonfinite(lse) == 0
+    rows = sample_rows(w, 384, np.random.default_rng(44))
+    ro, rl = attn_fp64(q, k, v, w.scale, w.causal, rows=rows)
+    go, gl = gather_rows(o, lse, w, rows)
+    err = rel_rmse(go, ro)
+    say("c4 sampled rel_rmse", err)
+    assert err <= REL_RMSE_MAX
+    assert lse_ok(gl, rl)
+
+
+def test_stress_jump_above_fp16_range(pasa):
+    # keys jump from bias 2 to bias 60 half way: unscaled scores ~2.3e5
+    w = W.custom(1, 512, 512, 4, 1, 128, True, kind="jump", seed=77, jump_at=200)
+    (q, k, v), o, lse = run_fwd(pasa, w)
+    ro, rl = attn_fp64(q, k, v, w.scale, True)
+    assert nonfinite(o) == 0
+    err = rel_rmse(o, ro)
+    say("jump rel_rmse", err)
+    assert err <= REL_RMSE_MAX
+    assert lse_ok(lse, rl)
+
+
+def test_resonance_per_row_phase_stress(pasa):
+    w = W.custom(1, 1024, 1024, 2, 2, 64, False, kind="resonance", seed=31, amp=48.0,
+                 period=64, flip_at=512, per_row_phase=True)
+    (q, k, v), o, lse = run_fwd(pasa, w)
+    ro, rl = attn_fp64(q, k, v, w.scale, False)
+    assert nonfinite(o) == 0
+    err = rel_rmse(o, ro)
+    say("per-row-phase resonance rel_rmse", err)
+    assert err <= REL_RMSE_MAX
+
+
+def test_deterministic(pasa):
+    w = W.custom(1, 300, 300, 7, 1, 128, True, kind="bias", seed=5, bias=30.0)
+    _, o1, l1 = run_fwd(pasa, w)
+    _, o2, l2 = run_fwd(pasa, w)
+    assert np.array_equal(o1.view(np.uint16), o2.view(np.uint16))
+    assert np.array_equal(l1, l2)
+
+
+# ----------------------------------------------------------------- naive kernel
+def test_naive_matches_oracle_without_overflow(pasa):
+    w = W.CONFIGS["c1"]
+    (q, k, v), o, lse = run_fwd(pasa, w, naive=True)
+    ro, rl = attn_fp64(q, k, v, w.scale, w.causal)
+    err = rel_rmse(o, ro)
+    say("naive c1 rel_rmse", err)
+    assert nonfinite(o) == 0
+    assert err <= 5e-3   # unscaled fp16 scores lose ~4 bits more than PASA's tile
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_naive_overflows_where_pasa_does_not(pasa, name):
+    w = W.CONFIGS[name]
+    (_, _, _), o, _ = run_fwd(pasa, w, naive=True)
+    bad = nonfinite(o)
+    say(name, "naive non-finite outputs:", bad, "of", o.size)
+    assert bad > 0
+
+
+# ----------------------------------------------------------------- decode
+def test_c5_decode_vs_oracle(pasa):
+    import torch
+    w = W.CONFIGS["c5"]
+    say("config c5 decode")
+    q, k, v = W.generate(w)
+    tq, tk, tv = to_gpu(q, k, v)
+    o, lse = pasa.attn_decode(tq, tk, tv, scale=w.scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    ro, rl = attn_fp64(q, k, v, w.scale, False)
+    err = rel_rmse(o, ro)
+    say("c5 rel_rmse", err, "nonfinite", nonfinite(o))
+    assert nonfinite(o) == 0 and nonfinite(lse) == 0
+    assert err <= REL_RMSE_MAX
+    assert lse_ok(lse, rl[:, :, 0])
+
+
+@pytest.mark.parametrize("Skv,n,Hq,Hkv,D", [(1, 0, 4, 1, 128), (129, 3, 7, 7, 64),
+                                            (1000, 0, 28, 4, 128), (5000, 7, 40, 1, 64),
+                                            (8192, 1, 8, 8, 128), (300, 64, 14, 2, 128)])
+def test_decode_shapes_vs_oracle(pasa, Skv, n, Hq, Hkv, D):
+    import torch
+    w = W.custom(3, 1, Skv, Hq, Hkv, D, False, kind="bias", seed=Skv + n, bias=30.0)
+    q, k, v = W.generate(w)
+    tq, tk, tv = to_gpu(q, k, v)
+    o, lse = pasa.attn_decode(tq, tk, tv, num_splits=n, scale=w.scale)
+    torch.cuda.synchronize()
+    ro, rl = attn_fp64(q, k, v, w.scale, False)
+    err = rel_rmse(o.cpu().numpy(), ro)
+    say("decode", (Skv, n, Hq, Hkv, D), "rel_rmse", err)
+    assert err <= REL_RMSE_MAX
+    assert lse_ok(lse.cpu().numpy(), rl[:, :, 0])
+
+
+def test_decode_combine_entry_on_oracle_partials(pasa):
+    """pasa_attn_decode_combine fed with oracle partials over disjoint key
+    ranges must reproduce the unsplit oracle (up to fp32/fp16 rounding)."""
+    import torch
+    B, Skv, Hq, Hkv, D, n = 2, 700, 6, 2, 128, 5
+    w = W.custom(B, 1, Skv, Hq, Hkv, D, False, kind="bias", seed=3, bias=30.0)
+    q, k, v = W.generate(w)
+    bounds = [0, 100, 101, 350, 700, 700]          # includes an empty range
+    po = np.zeros((B, Hq, n, D))
+    pl = np.zeros((B, Hq, n))
+    for s in range(n):
+        a, e = bounds[s], bounds[s + 1]
+        if e == a:
+            pl[:, :, s] = -np.inf
+            continue
+        os_, ls = attn_fp64(q, k[:, a:e], v[:, a:e], w.scale)
+        po[:, :, s] = os_[:, 0]
+        pl[:, :, s] = ls[:, :, 0]
+    ro, rl = attn_fp64(q, k, v, w.scale)
+    oc, lc = combine_fp64(po.reshape(B * Hq, n, D), pl.reshape(B * Hq, n))
+    assert np.allclose(oc, ro[:, 0].reshape(B * Hq, D), atol=1e-12)
+    tpo = torch.from_numpy(po.astype(np.float32)).cuda()
+    tpl = torch.from_numpy(pl.astype(np.float32)).cuda()
+    o, lse = pasa.attn_decode_combine(tpo, tpl)
+    torch.cuda.synchronize()
+    err = rel_rmse(o.cpu().numpy(), ro)
+    say("combine rel_rmse", err)
+    assert err <= 1e-3
+    assert lse_ok(lse.cpu().numpy(), rl[:, :, 0], abs_tol=1e-4)
+
+
+# ----------------------------------------------------------------- ABI on GPU
+def test_error_writes_nothing(pasa):
+    import ctypes
+
+    import torch
+    lib = pasa.raw()
+    q = torch.zeros((1, 8, 2, 96), dtype=torch.float16, device="cuda")
+    o = torch.full_like(q, 7.0)
+    rc = lib.pasa_attn_fwd(q.data_ptr(), q.data_ptr(), q.data_ptr(), o.data_ptr(), None, 1, 8, 8,
+                           2, 1, 96, ctypes.c_float(0.1), 0, None)
+    torch.cuda.synchronize()
+    assert rc == -2
+    assert bool((o == 7.0).all())

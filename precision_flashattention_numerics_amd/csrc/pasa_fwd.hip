@@ -19,9 +19,15 @@
 //     softmax is already laid out as the B operand (no LDS round trip): the K
 //     rows are fed to the first product in a permuted order (bits 2 and 3 of
 //     the row index swapped) so that every lane's scores are 8 consecutive
-//     keys per 16-key chunk.  V is transposed while it is staged into LDS.
-//   * K and V tiles are double-buffered in LDS; the next tile's global loads
-//     are in flight while the current tile is processed.
+//     keys per 16-key chunk.
+//   * K and V tiles go straight from HBM into LDS (buffer_load ... lds, no
+//     staging registers; rows past the sequence end read as zero), stored
+//     row-major with XOR-swizzled 16-byte chunks.  V is consumed through the
+//     transposing LDS read of gfx950 (ds_read_b64_tr_b16), so it needs no
+//     transpose on the way in.  Two LDS stages: the next block's loads are in
+//     flight while the current block is processed.
+//   * Blocks that every row of a wave sees in full take a branch-free path;
+//     only the diagonal / ragged-tail blocks evaluate the mask.
 //
 // The per-block half-precision softmax (pseudo-average shift, refine, fp16
 // exponentials and sums) lives in pasa_tile.hpp.
@@ -35,23 +41,22 @@ namespace {
 
 constexpr int kBR = 128;      // query rows per workgroup (32 per wave)
 constexpr int kBC = 64;       // keys per block
-constexpr int kThreads = 256; // 4 waves
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
 
 template <int D>
-using FwdStager = Stager<D, kBC, kThreads>;
-
+constexpr int tile_halves() { return kBC * D; }
 template <int D>
-constexpr int fwd_smem_bytes() { return 2 * FwdStager<D>::STAGE_HALVES * 2; }
+constexpr int fwd_smem_bytes() { return 2 /*stages*/ * 2 /*K,V*/ * tile_halves<D>() * 2; }
 
 template <int D, bool CAUSAL, bool NAIVE>
-__global__ __launch_bounds__(kThreads) void fwd_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, _Float16* __restrict__ o, float* __restrict__ lse,
     int Sq, int Skv, int Hq, int group, float c, int n_qtiles) {
-    using ST = FwdStager<D>;
     constexpr int KK = D / 16;
     constexpr int DT = D / 32;
-    extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
+    extern __shared__ __attribute__((aligned(1024))) _Float16 smem[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -72,6 +77,10 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(
     const _Float16* qb = q + ((int64_t)b * Sq * Hq + hq) * D;
     const _Float16* kb = k + ((int64_t)b * Skv * Hkv + hkv) * D;
     const _Float16* vb = v + ((int64_t)b * Skv * Hkv + hkv) * D;
+    const uint32_t slab_bytes = (uint32_t)(((int64_t)(Skv - 1) * kv_stride + D) * 2);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb, slab_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vb, slab_bytes);
+    const uint32_t stride_b = (uint32_t)(kv_stride * 2);
 
     // ---- key range of this workgroup and of this lane's row
     const int64_t shift = (int64_t)Skv - Sq;   // bottom-right causal alignment
@@ -90,50 +99,57 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(
     const int wave_lim_lo = row_limit(q0 + 32 * w);
     const int wave_lim_hi = row_limit(q0 + 32 * w + 31);
 
+    auto stage_ptr = [&](int stage) { return smem + stage * 2 * tile_halves<D>(); };
+    auto issue = [&](int blk) {
+        _Float16* st = stage_ptr(blk & 1);
+        stage_tile<D, kBC, kWaves, false>(krs, stride_b, blk * kBC, st, w, lane);
+        stage_tile<D, kBC, kWaves, true>(vrs, stride_b, blk * kBC, st + tile_halves<D>(), w, lane);
+    };
+    if (nblocks > 0) issue(0);
+
     // ---- Q operand: lane holds Q[qi][16*kk + 8*hh .. +7]
     h8 qreg[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
         qreg[kk] = qi < Sq ? *(const h8*)(qb + (int64_t)qi * q_stride + 16 * kk + 8 * hh) : (h8){};
 
-    ST stager;
     RowState st;
     f16v acc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = (f16v){};
 
-    if (nblocks > 0) {
-        stager.load(kb, vb, kv_stride, 0, Skv, tid);
-        stager.store(smem, tid);
-    }
+    wait_vmem();
     __syncthreads();
 
     for (int blk = 0; blk < nblocks; ++blk) {
-        const int stage = blk & 1;
-        if (blk + 1 < nblocks) stager.load(kb, vb, kv_stride, (blk + 1) * kBC, Skv, tid);
+        if (blk + 1 < nblocks) issue(blk + 1);
 
         const int kbase = blk * kBC;
         if (kbase < wave_lim_hi) {   // some row of this wave sees a key of the block
-            const _Float16* Ks = smem + stage * ST::STAGE_HALVES;
-            const _Float16* Vt = Ks + ST::K_HALVES;
+            const _Float16* Ks = stage_ptr(blk & 1);
+            const _Float16* Vs = Ks + tile_halves<D>();
             f16v S[2];
-            S[0] = qk_subtile<D, ST::KPAD>(Ks, 0, qreg, n, hh);
-            S[1] = qk_subtile<D, ST::KPAD>(Ks, 32, qreg, n, hh);
+            S[0] = qk_subtile_sw<D>(Ks, 0, qreg, n, hh);
+            S[1] = qk_subtile_sw<D>(Ks, 32, qreg, n, hh);
 
-            const bool full = kbase + kBC <= wave_lim_lo;
-            const int cnt = full ? kBC : max(0, min(kBC, lim - kbase));
-            auto vis = [&](int t, int r) { return kbase + 32 * t + key_of(r, hh) < lim; };
             h2 P[16];
-            const _Float16 alpha = softmax_block<2, NAIVE>(S, P, st, c, full, cnt, vis);
+            _Float16 alpha;
+            if (kbase + kBC <= wave_lim_lo) {   // the whole block is visible to the wave
+                alpha = softmax_block<2, NAIVE>(S, P, st, c, true, kBC, [](int, int) { return true; });
+            } else {
+                const int m = lim - kbase;        // keys [0, m) of the block are visible
+                const int cnt = max(0, min(kBC, m));
+                alpha = softmax_block<2, NAIVE>(S, P, st, c, false, cnt,
+                                                [&](int t, int r) { return 32 * t + key_of(r, hh) < m; });
+            }
             if (wave_any(alpha != (_Float16)1)) {
                 const float af = (float)alpha;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) acc[dt] *= af;
             }
-            pv_chunks<D, ST::VPAD, 4>(Vt, 0, P, acc, n, hh);
+            pv_chunks_tr<D, 4>(Vs, 0, P, acc, lane);
         }
-
-        if (blk + 1 < nblocks) stager.store(smem + (stage ^ 1) * ST::STAGE_HALVES, tid);
+        wait_vmem();
         __syncthreads();
     }
 

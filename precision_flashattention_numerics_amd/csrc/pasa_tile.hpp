@@ -254,6 +254,107 @@ struct Stager {
     }
 };
 
+// ---------------------------------------------------------------------------
+// Direct HBM -> LDS staging (buffer_load ... lds) with XOR-swizzled 16-byte
+// chunks, and the matching operand reads.
+//
+// A tile is ROWS keys x D columns of fp16, stored row-major without padding;
+// row r's 16-byte chunk c lives at chunk slot r*C + (c ^ swz(r)), C = D/8.
+// K tiles use swz_k (conflict-free 16-byte reads of 16 different rows at one
+// chunk); V tiles use swz_v (conflict-free transposing 8-byte reads of 4
+// consecutive rows x 4 consecutive chunks).
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    // Raw buffer: stride 0, bounds = bytes; reads past the bound return zero.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+    constexpr int C = D / 8;
+    return (r / (16 / C)) % C;
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+    constexpr int C = D / 8;
+    return 4 * ((r / (16 / C)) % (C / 4));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4 lds_s4;
+
+// Issue the loads of keys [row0, row0 + ROWS) of one head's K or V slab into
+// an LDS tile; the WAVES waves of the workgroup split the 1 KB segments.
+// stride_b = bytes between consecutive keys of the slab.
+template <int D, int ROWS, int WAVES, bool IS_V>
+__device__ __forceinline__ void stage_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t stride_b, int row0,
+                                           _Float16* tile, int w, int lane) {
+    constexpr int C = D / 8;
+    constexpr int SEGS = ROWS * C / 64;          // 1 KB segments in the tile
+    static_assert(SEGS % WAVES == 0, "segments must split evenly over waves");
+#pragma unroll
+    for (int i = 0; i < SEGS / WAVES; ++i) {
+        const int seg = w * (SEGS / WAVES) + i;
+        const int slot = seg * 64 + lane;
+        const int row = slot / C, pos = slot % C;
+        const int chunk = pos ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
+        const uint32_t off = (uint32_t)(row0 + row) * stride_b + (uint32_t)chunk * 16u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + seg * 512), 16, off, 0, 0,
+                                                 0);
+    }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// A operand of S^T = K Q^T: K row (row0 + sigma(n)), columns 16*kk + 8*hh..+7.
+template <int D>
+__device__ __forceinline__ f16v qk_subtile_sw(const _Float16* Ks, int row0, const h8 (&qreg)[D / 16],
+                                              int n, int hh) {
+    f16v s = (f16v){};
+    const int row = row0 + sigma(n);
+    const _Float16* base = Ks + row * D;
+    const int sw = swz_k<D>(row);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+        s = mfma_32x32x16(*(const h8*)(base + 8 * ((2 * kk + hh) ^ sw)), qreg[kk], s);
+    return s;
+}
+
+// O^T += V^T P^T for the 16-key chunks [ch0, ch0 + NCH) of a V tile.  The A
+// operand (head-dim row 32*dt + l%32, keys 16*ch + 8*hh + 0..7) is assembled
+// from two transposing LDS reads: in each 16-lane group, lane j receives
+// element (j % 4) of what lane 4*e + j/4 addressed, for e = 0..3; lane
+// 4*e + q addresses key (base + e), columns 4*q .. 4*q+3 of its group's 16.
+template <int D, int NCH>
+__device__ __forceinline__ void pv_chunks_tr(const _Float16* Vs, int ch0, const h2* P,
+                                             f16v (&acc)[D / 32], int lane) {
+    const int hh = lane >> 5;
+    const int g2 = (lane >> 4) & 1;
+    const int e = (lane >> 2) & 3;
+    const int q = lane & 3;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        const h2 p0 = P[4 * ch + 0], p1 = P[4 * ch + 1], p2 = P[4 * ch + 2], p3 = P[4 * ch + 3];
+        const h8 bp = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+        const int rowa = 16 * (ch0 + ch) + 8 * hh + e;   // keys +0..3
+        const int rowb = rowa + 4;                        // keys +4..7
+        const int swa = swz_v<D>(rowa), swb = swz_v<D>(rowb);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const int c = 4 * dt + 2 * g2 + (q >> 1);
+            const _Float16* pa = Vs + rowa * D + 8 * (c ^ swa) + 4 * (q & 1);
+            const _Float16* pb = Vs + rowb * D + 8 * (c ^ swb) + 4 * (q & 1);
+            const s4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)pa);
+            const s4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)pb);
+            const h4 ha = __builtin_bit_cast(h4, va), hb = __builtin_bit_cast(h4, vb);
+            const h8 a = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+            acc[dt] = mfma_32x32x16(a, bp, acc[dt]);
+        }
+    }
+}
+
 // S^T (32 keys x 32 query columns) for the keys at rows [row0, row0+32) of
 // the staged K tile; qreg is the B operand (query column l%32, 8 columns of
 // the head dimension per 16-wide contraction step).

@@ -43,7 +43,21 @@ def parse():
                     help="skip the oracle timing and the sampled parity check")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times "
+                         "(reference for the HBM byte counters), then exit")
     return ap.parse_args()
+
+
+def calibrate_copy(mib):
+    """A plain copy kernel of known size: reads and writes exactly mib MiB."""
+    import torch
+    src = torch.ones(mib * (1 << 20) // 2, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": mib * (1 << 20)}), flush=True)
 
 
 def main():
@@ -52,6 +66,10 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(every workload here fits one MI355X); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import numpy as np
     import torch

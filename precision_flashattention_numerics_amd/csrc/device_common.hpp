@@ -51,6 +51,44 @@ __device__ __forceinline__ h2 hexp2(h2 x) {
 
 __device__ __forceinline__ h2 hmax(h2 a, h2 b) { return __builtin_elementwise_max(a, b); }
 
+// exp2 of both halves of four packed pairs, written in place (no repacking):
+// v_exp_f16 on the low halves, then its SDWA form on the high halves, which
+// preserves the low result.  The preserving write reads the register a
+// transcendental instruction just wrote, a read that needs wait states on
+// this ISA; issuing the four low halves first puts three instructions
+// between each pair, and the trailing s_nop covers the first consumer.
+__device__ __forceinline__ void hexp2_pk4(const h2* x, h2* r) {
+    asm("v_exp_f16_e32 %0, %4\n\t"
+        "v_exp_f16_e32 %1, %5\n\t"
+        "v_exp_f16_e32 %2, %6\n\t"
+        "v_exp_f16_e32 %3, %7\n\t"
+        "v_exp_f16_sdwa %0, %4 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
+        "v_exp_f16_sdwa %1, %5 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
+        "v_exp_f16_sdwa %2, %6 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
+        "v_exp_f16_sdwa %3, %7 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
+        "s_nop 1"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+}
+
+// fp16(c * a + z) for two fp32 values, one rounding each (fused multiply-add
+// in mixed precision, round-to-nearest-even), packed into one register.
+__device__ __forceinline__ h2 fma_to_h2(float a, float b, float c, float z) {
+    h2 t;
+    asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[0,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %4, %2, %3 op_sel_hi:[0,0,0]"
+        : "=&v"(t)
+        : "v"(a), "v"(c), "v"(z), "v"(b));
+    return t;
+}
+
+// fp16(c * a + z), the same single rounding as fma_to_h2.
+__device__ __forceinline__ _Float16 fma_to_h(float a, float c, float z) {
+    h2 t;
+    asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[0,0,0]" : "=v"(t) : "v"(a), "v"(c), "v"(z));
+    return t.x;
+}
+
 // Two floats rounded to fp16 (round-to-nearest-even) and packed.
 __device__ __forceinline__ h2 to_h2(float a, float b) {
     return __builtin_convertvector((float __attribute__((ext_vector_type(2)))){a, b}, h2);

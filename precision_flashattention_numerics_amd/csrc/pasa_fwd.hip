@@ -9,12 +9,19 @@
 // shifts ("global recovering") so the normalisation and the log-sum-exp are
 // exact up to rounding.
 //
-// Work decomposition (one workgroup = 4 waves = 128 query rows of one head):
+// Work decomposition (one workgroup = 8 waves = 256 query rows of one head):
+//   * Two groups of four waves (rows 0-127 and 128-255 of the tile) share the
+//     K/V tiles in LDS and run in ping-pong: while one group issues its matrix
+//     products for a key block (P V of the previous block, then S^T = K Q^T of
+//     this one), the other group runs the half-precision softmax of its
+//     current block, and at every barrier they swap.  Each SIMD holds one wave
+//     of each group, so the matrix cores and the vector ALUs stay busy at the
+//     same time; the wave in its matrix phase runs at raised priority.
 //   * S^T = K Q^T on the matrix cores (v_mfma_f32_32x32x16_f16).  Q is the B
 //     operand and stays in registers for the whole key loop; K rows come from
-//     LDS.  With keys on the M side, each lane ends up holding 32 of the 64
-//     scores of ONE query row per key block, so row max / sum / mean are
-//     in-lane reductions plus a single exchange with the lane 32 apart.
+//     LDS.  With keys on the M side, each lane holds 32 of the 64 scores of ONE
+//     query row per key block, so row reductions are in-lane plus a single
+//     exchange with the lane 32 apart.
 //   * O^T += V^T P^T on the matrix cores.  The fp16 P tile produced by the
 //     softmax is already laid out as the B operand (no LDS round trip): the K
 //     rows are fed to the first product in a permuted order (bits 2 and 3 of
@@ -23,9 +30,10 @@
 //   * K and V tiles go straight from HBM into LDS (buffer_load ... lds, no
 //     staging registers; rows past the sequence end read as zero), stored
 //     row-major with XOR-swizzled 16-byte chunks.  V is consumed through the
-//     transposing LDS read of gfx950 (ds_read_b64_tr_b16), so it needs no
-//     transpose on the way in.  Two LDS stages: the next block's loads are in
-//     flight while the current block is processed.
+//     transposing LDS read of gfx950 (ds_read_b64_tr_b16).  Two LDS stages per
+//     tensor; each block's loads have two phases to land.
+//   * Workgroups are ordered so that each XCD (each with its own L2) works on
+//     one key/value head at a time, and causal tiles are issued longest first.
 //   * Blocks that every row of a wave sees in full take a branch-free path;
 //     only the diagonal / ragged-tail blocks evaluate the mask.
 //
@@ -39,21 +47,52 @@ namespace pasa {
 
 namespace {
 
-constexpr int kBR = 128;      // query rows per workgroup (32 per wave)
+constexpr int kBR = 256;      // query rows per workgroup (32 per wave)
 constexpr int kBC = 64;       // keys per block
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kXcds = 8;      // XCDs of an MI355X; workgroups are dealt round-robin
 
 template <int D>
 constexpr int tile_halves() { return kBC * D; }
 template <int D>
 constexpr int fwd_smem_bytes() { return 2 /*stages*/ * 2 /*K,V*/ * tile_halves<D>() * 2; }
 
+// Work item of workgroup L: (batch, query head, query tile).  Items are
+// enumerated key/value head by key/value head, longest causal tile first,
+// and dealt to XCDs so that each XCD holds one key/value head (or one slice
+// of one) at a time when the counts allow it.
+struct Item { int b, hq, tile; };
+__device__ __forceinline__ Item decode_item(int L, int N, int B, int Hq, int g, int nt, bool causal) {
+    const int Hkv = Hq / g;
+    const int U = B * Hkv;            // key/value units
+    const int per_unit = g * nt;
+    int unit, item;
+    if (N % kXcds == 0 && kXcds % U == 0 && per_unit % (kXcds / U) == 0) {
+        const int X = kXcds / U, xcd = L % kXcds, k = L / kXcds;
+        unit = xcd / X;
+        item = k * X + xcd % X;
+    } else if (U % kXcds == 0) {
+        const int xcd = L % kXcds, k = L / kXcds;
+        unit = (k / per_unit) * kXcds + xcd;
+        item = k % per_unit;
+    } else {
+        unit = L / per_unit;
+        item = L % per_unit;
+    }
+    const int rank = item / g;
+    Item it;
+    it.b = unit / Hkv;
+    it.hq = (unit % Hkv) * g + item % g;
+    it.tile = causal ? nt - 1 - rank : rank;
+    return it;
+}
+
 template <int D, bool CAUSAL, bool NAIVE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, _Float16* __restrict__ o, float* __restrict__ lse,
-    int Sq, int Skv, int Hq, int group, float c, int n_qtiles) {
+    int B, int Sq, int Skv, int Hq, int group, float c, int n_qtiles) {
     constexpr int KK = D / 16;
     constexpr int DT = D / 32;
     extern __shared__ __attribute__((aligned(1024))) _Float16 smem[];
@@ -61,16 +100,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
+    const int grp = w >> 2;     // ping-pong group (wave-uniform)
     const int hh = lane >> 5;   // which half of the wave
     const int n = lane & 31;    // query column owned by this lane
 
-    const int hq = blockIdx.x;
-    const int tile = CAUSAL ? (n_qtiles - 1 - (int)blockIdx.y) : (int)blockIdx.y;
-    const int b = blockIdx.z;
+    const Item it = decode_item(blockIdx.x, gridDim.x, B, Hq, group, n_qtiles, CAUSAL);
+    const int hq = it.hq, b = it.b;
     const int Hkv = Hq / group;
     const int hkv = hq / group;
-    const int q0 = tile * kBR;
-    const int qi = q0 + 32 * w + n;
+    const int q0 = it.tile * kBR;
+    const int wrow0 = q0 + 32 * w;      // first query row of this wave
+    const int qi = wrow0 + n;
 
     const int64_t q_stride = (int64_t)Hq * D;
     const int64_t kv_stride = (int64_t)Hkv * D;
@@ -78,8 +118,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const _Float16* kb = k + ((int64_t)b * Skv * Hkv + hkv) * D;
     const _Float16* vb = v + ((int64_t)b * Skv * Hkv + hkv) * D;
     const uint32_t slab_bytes = (uint32_t)(((int64_t)(Skv - 1) * kv_stride + D) * 2);
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kb, slab_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vb, slab_bytes);
+    const i32x4 krs = make_rsrc(kb, slab_bytes);
+    const i32x4 vrs = make_rsrc(vb, slab_bytes);
     const uint32_t stride_b = (uint32_t)(kv_stride * 2);
 
     // ---- key range of this workgroup and of this lane's row
@@ -96,16 +136,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         return (int)max<int64_t>(0, min<int64_t>(Skv, l));
     };
     const int lim = row_limit(qi);
-    const int wave_lim_lo = row_limit(q0 + 32 * w);
-    const int wave_lim_hi = row_limit(q0 + 32 * w + 31);
+    const int wave_lim_lo = row_limit(wrow0);
+    const int wave_lim_hi = row_limit(wrow0 + 31);
+    auto active = [&](int blk) { return blk < nblocks && blk * kBC < wave_lim_hi; };
 
-    auto stage_ptr = [&](int stage) { return smem + stage * 2 * tile_halves<D>(); };
-    auto issue = [&](int blk) {
-        _Float16* st = stage_ptr(blk & 1);
-        stage_tile<D, kBC, kWaves, false>(krs, stride_b, blk * kBC, st, w, lane);
-        stage_tile<D, kBC, kWaves, true>(vrs, stride_b, blk * kBC, st + tile_halves<D>(), w, lane);
+    _Float16* const Kst = smem;                           // 2 stages of K
+    _Float16* const Vst = smem + 2 * tile_halves<D>();    // 2 stages of V
+    auto load_k = [&](int blk) {
+        stage_tile<D, kBC, kWaves, false>(krs, stride_b, blk * kBC,
+                                          Kst + (blk & 1) * tile_halves<D>(), w, lane);
     };
-    if (nblocks > 0) issue(0);
+    auto load_v = [&](int blk) {
+        stage_tile<D, kBC, kWaves, true>(vrs, stride_b, blk * kBC,
+                                         Vst + (blk & 1) * tile_halves<D>(), w, lane);
+    };
+    if (nblocks > 0) load_k(0);
 
     // ---- Q operand: lane holds Q[qi][16*kk + 8*hh .. +7]
     h8 qreg[KK];
@@ -117,39 +162,59 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     f16v acc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = (f16v){};
+    f16v S[2];
+    h2 P[16];
+
+    // matrix phase of block j: P V for block j-1, then S^T = K Q^T for block j
+    auto mphase = [&](int j) {
+        __builtin_amdgcn_s_setprio(1);
+        if (j >= 1 && active(j - 1)) pv_chunks_tr<D, 4>(Vst + ((j - 1) & 1) * tile_halves<D>(), 0, P, acc, lane);
+        if (active(j)) {
+            const _Float16* Ks = Kst + (j & 1) * tile_halves<D>();
+            S[0] = qk_subtile_sw<D>(Ks, 0, qreg, n, hh);
+            S[1] = qk_subtile_sw<D>(Ks, 32, qreg, n, hh);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+    // vector phase of block j: half-precision softmax, accumulator rescale
+    auto vphase = [&](int j) {
+        if (!active(j)) return;
+        const int kbase = j * kBC;
+        _Float16 alpha;
+        if (kbase + kBC <= wave_lim_lo) {   // the whole block is visible to the wave
+            alpha = softmax_block<2, NAIVE>(S, P, st, c, true, kBC, [](int, int) { return true; });
+        } else {
+            const int m = lim - kbase;        // keys [0, m) of the block are visible
+            const int cnt = max(0, min(kBC, m));
+            alpha = softmax_block<2, NAIVE>(S, P, st, c, false, cnt,
+                                            [&](int t, int r) { return 32 * t + key_of(r, hh) < m; });
+        }
+        if (wave_any(alpha != (_Float16)1)) {
+            const float af = (float)alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= af;
+        }
+    };
 
     wait_vmem();
     __syncthreads();
 
-    for (int blk = 0; blk < nblocks; ++blk) {
-        if (blk + 1 < nblocks) issue(blk + 1);
-
-        const int kbase = blk * kBC;
-        if (kbase < wave_lim_hi) {   // some row of this wave sees a key of the block
-            const _Float16* Ks = stage_ptr(blk & 1);
-            const _Float16* Vs = Ks + tile_halves<D>();
-            f16v S[2];
-            S[0] = qk_subtile_sw<D>(Ks, 0, qreg, n, hh);
-            S[1] = qk_subtile_sw<D>(Ks, 32, qreg, n, hh);
-
-            h2 P[16];
-            _Float16 alpha;
-            if (kbase + kBC <= wave_lim_lo) {   // the whole block is visible to the wave
-                alpha = softmax_block<2, NAIVE>(S, P, st, c, true, kBC, [](int, int) { return true; });
-            } else {
-                const int m = lim - kbase;        // keys [0, m) of the block are visible
-                const int cnt = max(0, min(kBC, m));
-                alpha = softmax_block<2, NAIVE>(S, P, st, c, false, cnt,
-                                                [&](int t, int r) { return 32 * t + key_of(r, hh) < m; });
-            }
-            if (wave_any(alpha != (_Float16)1)) {
-                const float af = (float)alpha;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) acc[dt] *= af;
-            }
-            pv_chunks_tr<D, 4>(Vs, 0, P, acc, lane);
+    // Phase p: group 0 runs mphase(p/2) on even p and vphase(p/2) on odd p;
+    // group 1 runs one phase behind.  K(m+1) and V(m) are loaded during phases
+    // 2m and 2m+1 into the stages freed by K(m-1) and V(m-2).
+    const int nphase = nblocks > 0 ? 2 * nblocks + 2 : 0;
+    for (int p = 0; p < nphase; ++p) {
+        if ((p & 1) == 0) {
+            const int m = p >> 1;
+            if (m + 1 < nblocks) load_k(m + 1);
+            if (m < nblocks) load_v(m);
         }
-        wait_vmem();
+        const int pp = p - grp;   // this group's own phase index
+        if (pp >= 0) {
+            if ((pp & 1) == 0) mphase(pp >> 1);
+            else vphase(pp >> 1);
+        }
+        if (p & 1) wait_vmem();
         __syncthreads();
     }
 
@@ -180,12 +245,10 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     const int n_qtiles = (a.seqlen_q + kBR - 1) / kBR;
-    // x = query head, y = query tile: consecutive workgroups are the heads of
-    // one tile, and for causal masking tiles are issued longest first.
-    dim3 grid(a.num_heads_q, n_qtiles, a.batch);
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, stream,
+    const int64_t n_items = (int64_t)a.batch * a.num_heads_q * n_qtiles;
+    hipLaunchKernelGGL(kern, dim3((unsigned)n_items), dim3(kThreads), smem, stream,
                        (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
-                       (_Float16*)a.o, a.lse, a.seqlen_q, a.seqlen_kv, a.num_heads_q,
+                       (_Float16*)a.o, a.lse, a.batch, a.seqlen_q, a.seqlen_kv, a.num_heads_q,
                        a.gqa_group, a.softmax_scale * kLog2e, n_qtiles);
     return hipGetLastError();
 }

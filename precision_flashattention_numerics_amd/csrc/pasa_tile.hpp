@@ -9,11 +9,11 @@
 //
 //   mu    = mean of the row's visible scores S in the block         (fp32)
 //   off   = c*mu on the row's first visible block, else max(c*mu, R) (fp32)
-//   T     = fp16_rne(c*S - off), masked keys -> -inf                  (fp16)
+//   T     = fp16_rne(c*S - off) (one rounding), masked keys -> -inf   (fp16)
 //   m_b   = max_j T                                                   (fp16)
-//   if m_b > THETA (the tile's largest entries sit where fp16 is
-//   coarse, or overflowed): off = max_j c*S over visible keys, and T,
-//   m_b are recomputed                                                (rare)
+//   if m_b > THETA (the tile's largest entries would sit where fp16 is
+//   coarse, or overflow): off = max_j c*S over visible keys, and T, m_b
+//   are taken relative to that instead
 //   R'    = max(R, off + m_b)      running maximum, log2 units        (fp32)
 //   s     = fp16(R' - off);  P = exp2(T - s);  r = sum_j P            (fp16)
 //   alpha = exp2(fp16(R - R'))                                        (fp16)
@@ -77,6 +77,12 @@ struct RowState {
 //   vis     vis(t, r) -> visibility of that key (used only when !full)
 // Writes P (packed fp16 pairs, P[8*t + r/2] = keys r, r+1 of sub-tile t) and
 // returns alpha, the factor the caller applies to its accumulator.
+//
+// The tile maximum m_b = max_j fp16(c*S_j - off) equals fp16(c*max_j S_j - off)
+// because rounding to fp16 is monotone; it is therefore taken from one fp32
+// max pass that runs beside the pseudo-average sum, and the refine decision
+// (m_b > THETA -> centre at the row maximum) is made before the fp16 tile is
+// formed, so the tile is formed exactly once and without a branch.
 template <int NT, bool NAIVE, typename Vis>
 __device__ __forceinline__ _Float16 softmax_block(const f16v (&S)[NT], h2 (&P)[8 * NT],
                                                   RowState& st, float c, bool full, int cnt,
@@ -85,47 +91,38 @@ __device__ __forceinline__ _Float16 softmax_block(const f16v (&S)[NT], h2 (&P)[8
     _Float16 mb;
     float off = 0.0f;
     if (!NAIVE) {
-        float sum = 0.0f;
+        float sum = 0.0f, m32 = -__builtin_inff();
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sum += (full || vis(t, r)) ? S[t][r] : 0.0f;
+            for (int r = 0; r < 16; ++r) {
+                const bool on = full || vis(t, r);
+                sum += on ? S[t][r] : 0.0f;
+                m32 = fmaxf(m32, on ? S[t][r] : -__builtin_inff());
+            }
         sum += xor32(sum);
+        m32 = fmaxf(m32, xor32(m32));
         const float cmu = cnt > 0 ? c * (sum / (float)cnt) : st.R;
         off = (st.R == -__builtin_inff()) ? cmu : fmaxf(cmu, st.R);
-
-        auto make_tile = [&](float o) -> _Float16 {
-            h2 mm = (h2){kHalfNegInf, kHalfNegInf};
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    h2 x = to_h2(__builtin_fmaf(c, S[t][r], -o), __builtin_fmaf(c, S[t][r + 1], -o));
-                    if (!full) {
-                        if (!vis(t, r)) x.x = kHalfNegInf;
-                        if (!vis(t, r + 1)) x.y = kHalfNegInf;
-                    }
-                    T[8 * t + r / 2] = x;
-                    mm = hmax(mm, x);
-                }
-            _Float16 m = mm.x > mm.y ? mm.x : mm.y;
-            _Float16 p = xor32(m);
-            return m > p ? m : p;
-        };
-        mb = make_tile(off);
-        // NaN-safe: an overflowed (+inf) or NaN maximum also triggers it
-        const bool need = cnt > 0 && !(mb <= (_Float16)kTheta);
-        if (wave_any(need)) {
-            float m32 = -__builtin_inff();
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (full || vis(t, r)) m32 = fmaxf(m32, S[t][r]);
-            m32 = fmaxf(m32, xor32(m32));
-            if (need) off = c * m32;
-            mb = make_tile(off);
+        mb = fma_to_h(m32, c, -off);
+        // refine: the tile's largest entries would sit where fp16 is coarse
+        // (or overflow); centre the row at its own maximum instead
+        if (cnt > 0 && !(mb <= (_Float16)kTheta)) {
+            off = c * m32;
+            mb = fma_to_h(m32, c, -off);
         }
+        const float noff = -off;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                h2 x = fma_to_h2(S[t][r], S[t][r + 1], c, noff);
+                if (!full) {
+                    if (!vis(t, r)) x.x = kHalfNegInf;
+                    if (!vis(t, r + 1)) x.y = kHalfNegInf;
+                }
+                T[8 * t + r / 2] = x;
+            }
     } else {
         const _Float16 ch = (_Float16)c;
         h2 mm = (h2){kHalfNegInf, kHalfNegInf};
@@ -150,7 +147,9 @@ __device__ __forceinline__ _Float16 softmax_block(const f16v (&S)[NT], h2 (&P)[8
     const _Float16 s = cnt > 0 ? (_Float16)(Rn - off) : (_Float16)0;
     const h2 s2 = {s, s};
 #pragma unroll
-    for (int i = 0; i < 8 * NT; ++i) P[i] = hexp2(T[i] - s2);
+    for (int i = 0; i < 8 * NT; ++i) T[i] = T[i] - s2;
+#pragma unroll
+    for (int i = 0; i < 8 * NT; i += 4) hexp2_pk4(T + i, P + i);
 
     // fp16 pairwise tree sum of the lane's exponentials, then across halves
     h2 a[4 * NT];
@@ -264,10 +263,27 @@ struct Stager {
 // chunk); V tiles use swz_v (conflict-free transposing 8-byte reads of 4
 // consecutive rows x 4 consecutive chunks).
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    // Raw buffer: stride 0, bounds = bytes; reads past the bound return zero.
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (stride 0) over [base, base + bytes): reads past the
+// bound return zero, which is how ragged tails are padded.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    return (i32x4){(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+
+// One 16-byte-per-lane load from a buffer straight into LDS: lane l's bytes
+// land at lds + 16*l.  Issued as inline assembly on purpose: the compiler
+// would otherwise wait for every such load before any later LDS read (it
+// cannot tell the staging buffers apart); this kernel orders them itself with
+// an explicit vmcnt(0) wait and a barrier before the tile is consumed.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, const void* lds) {
+    const uint32_t la = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(la)
+                 : "memory", "m0");
 }
 
 template <int D>
@@ -289,7 +305,7 @@ typedef __attribute__((address_space(3))) s4 lds_s4;
 // an LDS tile; the WAVES waves of the workgroup split the 1 KB segments.
 // stride_b = bytes between consecutive keys of the slab.
 template <int D, int ROWS, int WAVES, bool IS_V>
-__device__ __forceinline__ void stage_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t stride_b, int row0,
+__device__ __forceinline__ void stage_tile(i32x4 rsrc, uint32_t stride_b, int row0,
                                            _Float16* tile, int w, int lane) {
     constexpr int C = D / 8;
     constexpr int SEGS = ROWS * C / 64;          // 1 KB segments in the tile
@@ -301,12 +317,13 @@ __device__ __forceinline__ void stage_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t
         const int row = slot / C, pos = slot % C;
         const int chunk = pos ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
         const uint32_t off = (uint32_t)(row0 + row) * stride_b + (uint32_t)chunk * 16u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + seg * 512), 16, off, 0, 0,
-                                                 0);
+        dma16(rsrc, off, tile + seg * 512);
     }
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima).  The builtin,
+// unlike an asm statement, also informs the compiler's own wait tracking.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // A operand of S^T = K Q^T: K row (row0 + sigma(n)), columns 16*kk + 8*hh..+7.
 template <int D>

@@ -25,15 +25,30 @@ __device__ __forceinline__ f16v mfma_32x32x16(h8 a, h8 b, f16v c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// Exchange with the lane 32 positions away (the other half of the wave).
-__device__ __forceinline__ float xor32(float x) {
-    return __int_as_float(__builtin_amdgcn_ds_bpermute(((int)__lane_id() ^ 32) << 2,
-                                                       __float_as_int(x)));
+// Reductions across the two halves of the wave (lanes l and l^32).
+// v_permlane32_swap(x, x) yields (x[l], x[l+32]) in lanes 0-31 and
+// (x[l-32], x[l]) in lanes 32-63, so combining its two results in that order
+// gives both lanes of a pair the identical, order-fixed value.
+__device__ __forceinline__ float xsum32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ _Float16 xor32(_Float16 x) {
-    unsigned short u = __builtin_bit_cast(unsigned short, x);
-    int r = __builtin_amdgcn_ds_bpermute(((int)__lane_id() ^ 32) << 2, (int)u);
-    return __builtin_bit_cast(_Float16, (unsigned short)r);
+__device__ __forceinline__ float xmax32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ _Float16 xsum32(_Float16 x) {
+    const unsigned u = __builtin_bit_cast(unsigned short, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(_Float16, (unsigned short)r[0]) +
+           __builtin_bit_cast(_Float16, (unsigned short)r[1]);
+}
+__device__ __forceinline__ _Float16 xmax32(_Float16 x) {
+    const unsigned u = __builtin_bit_cast(unsigned short, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const _Float16 a = __builtin_bit_cast(_Float16, (unsigned short)r[0]);
+    const _Float16 b = __builtin_bit_cast(_Float16, (unsigned short)r[1]);
+    return a > b ? a : b;
 }
 
 __device__ __forceinline__ bool wave_any(bool p) {

@@ -168,11 +168,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // matrix phase of block j: P V for block j-1, then S^T = K Q^T for block j
     auto mphase = [&](int j) {
         __builtin_amdgcn_s_setprio(1);
-        if (j >= 1 && active(j - 1)) pv_chunks_tr<D, 4>(Vst + ((j - 1) & 1) * tile_halves<D>(), 0, P, acc, lane);
-        if (active(j)) {
-            const _Float16* Ks = Kst + (j & 1) * tile_halves<D>();
+        const bool pv = j >= 1 && active(j - 1);
+        const bool qk = active(j);
+        const _Float16* Vs = Vst + ((j - 1) & 1) * tile_halves<D>();
+        const _Float16* Ks = Kst + (j & 1) * tile_halves<D>();
+        if (pv && qk) {
+            // one straight-line region of 2 * (16 * D / 64) products whose LDS
+            // operand reads are kept several products ahead of their use
+            pv_chunks_tr<D, 4>(Vs, 0, P, acc, lane);
             S[0] = qk_subtile_sw<D>(Ks, 0, qreg, n, hh);
             S[1] = qk_subtile_sw<D>(Ks, 32, qreg, n, hh);
+            constexpr int NMF = 2 * 4 * (D / 32) + 2 * (D / 16);   // products in the region
+            constexpr int NRD = 2 * 4 * (D / 32) + 2 * (D / 16);   // 2 reads per PV product, 1 per QK
+            constexpr int AHEAD = 8;
+            constexpr int STEADY = (NRD - AHEAD) / 2;
+            __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+            for (int i = 0; i < STEADY; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, NMF - STEADY, 0);
+        } else {
+            if (pv) pv_chunks_tr<D, 4>(Vs, 0, P, acc, lane);
+            if (qk) {
+                S[0] = qk_subtile_sw<D>(Ks, 0, qreg, n, hh);
+                S[1] = qk_subtile_sw<D>(Ks, 32, qreg, n, hh);
+            }
         }
         __builtin_amdgcn_s_setprio(0);
     };

@@ -91,17 +91,19 @@ __device__ __forceinline__ _Float16 softmax_block(const f16v (&S)[NT], h2 (&P)[8
     _Float16 mb;
     float off = 0.0f;
     if (!NAIVE) {
-        float sum = 0.0f, m32 = -__builtin_inff();
+        // four independent partial sums / maxima keep the dependency chains short
+        float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float pm[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const bool on = full || vis(t, r);
-                sum += on ? S[t][r] : 0.0f;
-                m32 = fmaxf(m32, on ? S[t][r] : -__builtin_inff());
+                ps[r & 3] += on ? S[t][r] : 0.0f;
+                pm[r & 3] = fmaxf(pm[r & 3], on ? S[t][r] : -__builtin_inff());
             }
-        sum += xor32(sum);
-        m32 = fmaxf(m32, xor32(m32));
+        const float sum = xsum32((ps[0] + ps[1]) + (ps[2] + ps[3]));
+        const float m32 = xmax32(fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3])));
         const float cmu = cnt > 0 ? c * (sum / (float)cnt) : st.R;
         off = (st.R == -__builtin_inff()) ? cmu : fmaxf(cmu, st.R);
         mb = fma_to_h(m32, c, -off);
@@ -138,9 +140,7 @@ __device__ __forceinline__ _Float16 softmax_block(const f16v (&S)[NT], h2 (&P)[8
                 T[8 * t + r / 2] = x;
                 mm = hmax(mm, x);
             }
-        _Float16 m = mm.x > mm.y ? mm.x : mm.y;
-        _Float16 p = xor32(m);
-        mb = m > p ? m : p;
+        mb = xmax32(mm.x > mm.y ? mm.x : mm.y);
     }
 
     const float Rn = cnt > 0 ? fmaxf(st.R, off + (float)mb) : st.R;
@@ -159,8 +159,7 @@ __device__ __forceinline__ _Float16 softmax_block(const f16v (&S)[NT], h2 (&P)[8
     for (int w = 2 * NT; w >= 1; w >>= 1)
 #pragma unroll
         for (int i = 0; i < w; ++i) a[i] = a[2 * i] + a[2 * i + 1];
-    _Float16 rsum = a[0].x + a[0].y;
-    rsum = rsum + xor32(rsum);
+    const _Float16 rsum = xsum32((_Float16)(a[0].x + a[0].y));
 
     const _Float16 alpha = cnt > 0 ? hexp2((_Float16)(st.R - Rn)) : (_Float16)1;
     if (!NAIVE)

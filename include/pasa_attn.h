@@ -108,8 +108,8 @@ int pasa_naive_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
  * Launches the split kernel and the combine kernel on `stream`, in order.
  * Errors: as pasa_attn_fwd (without the seqlen_kv bound), plus
  * PASA_ERR_WORKSPACE for a null, misaligned or too-small workspace, and
- * PASA_ERR_INVALID for num_splits < 0.  More splits than key blocks are
- * clamped to the number of 64-key blocks.
+ * PASA_ERR_INVALID for num_splits < 0.  More splits than 32-key sub-tiles
+ * are clamped to the number of sub-tiles.
  */
 int pasa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
                      float* lse, int batch, int seqlen_kv, int num_heads_q, int gqa_group,
@@ -118,7 +118,7 @@ int pasa_attn_decode(const void* q, const void* k_cache, const void* v_cache, vo
 
 /* The split count pasa_attn_decode uses for num_splits = 0 (host function, no
  * device work): enough (sequence, key/value head, split) work items to fill the
- * chip, clamped to the number of 64-key blocks.  Returns 0 on invalid sizes. */
+ * chip, clamped to the number of 32-key sub-tiles.  Returns 0 on invalid sizes. */
 int pasa_attn_decode_splits(int batch, int seqlen_kv, int num_heads_q, int gqa_group);
 
 /* Workspace size in bytes for pasa_attn_decode with num_splits splits (host

@@ -135,8 +135,7 @@ def decode_workspace(q, k_cache, num_splits=0):
     B, _, Hq, D = q.shape
     _, Skv, Hkv, _ = k_cache.shape
     n = num_splits or decode_splits(B, Skv, Hq, Hq // Hkv)
-    n = min(n, (Skv + 127) // 128)
-    nbytes = decode_workspace_bytes(B, Hq, D, n)
+    nbytes = decode_workspace_bytes(B, Hq, D, n)   # the library may use fewer splits
     ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=q.device)
     off = (-ws.data_ptr()) % 256
     return ws[off:off + nbytes], n

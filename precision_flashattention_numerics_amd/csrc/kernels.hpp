@@ -34,7 +34,7 @@ hipError_t launch_decode_combine(const float* o_part, const float* lse_part, voi
                                  int batch, int num_heads_q, int head_dim, int num_splits,
                                  hipStream_t stream);
 
-// Keys per split-kernel workgroup iteration; splits are whole multiples of it.
-constexpr int kDecodeBlock = 128;
+// Keys per decode sub-tile; splits are whole multiples of it.
+constexpr int kDecodeBlock = 32;
 
 }  // namespace pasa

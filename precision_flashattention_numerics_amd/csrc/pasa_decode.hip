@@ -3,23 +3,24 @@
 //
 // Method: the per-block half-precision softmax of "Online Pseudo-average
 // Shifting Attention (PASA) for Robust Low-precision LLM Inference", Abstract
-// (pasa_tile.hpp), applied to a contiguous key range per workgroup.  The
-// partials over disjoint key ranges are merged with their log-sum-exp weights:
-// the "Block Sparse Flash Attention" topic page, FoldAttention card, states
-// that softmax is invariant to a common shift and that normalised partials
-// over disjoint key ranges compose (split KV) without further rescaling.
+// (pasa_tile.hpp), applied to a contiguous key range per wave.  The partials
+// over disjoint key ranges are merged with their log-sum-exp weights: the
+// "Block Sparse Flash Attention" topic page, FoldAttention card, states that
+// softmax is invariant to a common shift and that normalised partials over
+// disjoint key ranges compose (split KV) without further rescaling.
 //
-// Split kernel: grid (num_splits, Hkv * head_chunks, batch), 4 waves.
-//   The workgroup owns keys [s*L, min((s+1)*L, Skv)) of one key/value head, L a
-//   multiple of 128.  The up to 32 query heads sharing that key/value head are
-//   the 32 query columns of S^T = K Q^T (unused columns are zero).  Each
-//   128-key block is staged into LDS by all 256 threads (K row-major, V
-//   transposed); wave w takes keys [32w, 32w+32) of every block with its own
-//   online-softmax state, and the four states are merged at the end in fp32.
-//   The next block's global loads are in flight while the current one is
-//   processed; decode is bound by streaming the KV cache from HBM.
-// Combine kernel: one workgroup per (batch, query head), one thread per
-//   head-dim column.
+// Split kernel: one wave per workgroup; the wave owns keys [s*L, (s+1)*L) of
+// one key/value head of one sequence (L a multiple of 32).  The up to 32
+// query heads sharing that key/value head are the 32 query columns of
+// S^T = K Q^T (unused columns are zero).  Decode reads every KV-cache byte
+// once, so the kernel is bound by HBM: each wave streams its keys in 32-key
+// sub-tiles straight from HBM into a private ring of LDS slots
+// (buffer_load ... lds), keeping the next sub-tiles in flight while it
+// computes on the current one; it synchronises only with itself
+// (s_waitcnt vmcnt), never with other waves.  Every wave writes one fp32
+// partial (o_s, lse_s).
+// Combine kernel: one workgroup per (sequence, query head), one thread per
+// head-dim column.
 
 #include "kernels.hpp"
 #include "pasa_tile.hpp"
@@ -28,41 +29,39 @@ namespace pasa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBK = kDecodeBlock;   // keys per staged block (32 per wave)
+constexpr int kSub = kDecodeBlock;   // keys per sub-tile (one 32x32 product tile)
+constexpr int kSlots = 3;            // LDS ring depth per wave
 
 template <int D>
-using DecStager = Stager<D, kBK, kThreads>;
+constexpr int sub_halves() { return kSub * D; }                     // one tensor, one sub-tile
+template <int D>
+constexpr int dec_smem_bytes() { return kSlots * 2 * sub_halves<D>() * 2; }
+template <int D>
+constexpr int dma_per_sub() { return 2 * (kSub * D / 8) / 64; }     // 16-byte-per-lane loads
 
 template <int D>
-constexpr int dec_smem_bytes() {
-    constexpr int stage = DecStager<D>::STAGE_HALVES * 2;
-    constexpr int merge = (4 * 32 * (D + 4) + 2 * 4 * 32) * 4;   // acc, R, L of the 4 waves
-    return stage > merge ? stage : merge;
-}
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(
+__global__ __launch_bounds__(64) void decode_split_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, float* __restrict__ o_part, float* __restrict__ lse_part,
-    int Skv, int Hq, int group, float c, int split_len, int head_chunks) {
-    using ST = DecStager<D>;
+    int Skv, int Hq, int group, float c, int split_len, int head_chunks, int nsplit) {
     constexpr int KK = D / 16;
     constexpr int DT = D / 32;
-    extern __shared__ __attribute__((aligned(16))) _Float16 smem[];
+    constexpr int NL = dma_per_sub<D>();
+    extern __shared__ __attribute__((aligned(1024))) _Float16 smem[];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int lane = threadIdx.x;
     const int hh = lane >> 5;
     const int n = lane & 31;
 
-    const int split = blockIdx.x;
-    const int nsplit = gridDim.x;
-    const int hkv = blockIdx.y / head_chunks;
-    const int hc = blockIdx.y % head_chunks;
-    const int b = blockIdx.z;
+    // workgroup -> (split, head chunk, key/value head, sequence), split fastest
+    int id = blockIdx.x;
+    const int split = id % nsplit;
+    id /= nsplit;
+    const int hc = id % head_chunks;
+    id /= head_chunks;
     const int Hkv = Hq / group;
+    const int hkv = id % Hkv;
+    const int b = id / Hkv;
     const int hloc = 32 * hc + n;             // query head within the group
     const bool row_valid = hloc < group;
     const int hq = hkv * group + hloc;
@@ -70,86 +69,86 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     const int64_t kv_stride = (int64_t)Hkv * D;
     const _Float16* kb = k + ((int64_t)b * Skv * Hkv + hkv) * D;
     const _Float16* vb = v + ((int64_t)b * Skv * Hkv + hkv) * D;
+    const uint32_t slab_bytes = (uint32_t)(((int64_t)(Skv - 1) * kv_stride + D) * 2);
+    const i32x4 krs = make_rsrc(kb, slab_bytes);
+    const i32x4 vrs = make_rsrc(vb, slab_bytes);
+    const uint32_t stride_b = (uint32_t)(kv_stride * 2);
 
     const int kbeg = min(split * split_len, Skv);
     const int kend = min(kbeg + split_len, Skv);
-    const int nblocks = (kend - kbeg + kBK - 1) / kBK;
+    const int nsub = (kend - kbeg + kSub - 1) / kSub;
+
+    auto slot_k = [&](int j) { return smem + (j % kSlots) * 2 * sub_halves<D>(); };
+    auto issue = [&](int j) {
+        _Float16* sk = slot_k(j);
+        stage_tile<D, kSub, 1, false>(krs, stride_b, kbeg + j * kSub, sk, 0, lane);
+        stage_tile<D, kSub, 1, true>(vrs, stride_b, kbeg + j * kSub, sk + sub_halves<D>(), 0, lane);
+    };
 
     h8 qreg[KK];
     const _Float16* qrow = q + ((int64_t)b * Hq + hq) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
         qreg[kk] = row_valid ? *(const h8*)(qrow + 16 * kk + 8 * hh) : (h8){};
+    wait_vmem();
 
-    ST stager;
+#pragma unroll
+    for (int j = 0; j < kSlots - 1; ++j)
+        if (j < nsub) issue(j);
+
     RowState st;
     f16v acc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = (f16v){};
 
-    if (nblocks > 0) stager.load(kb, vb, kv_stride, kbeg, kend, tid);
-    for (int blk = 0; blk < nblocks; ++blk) {
-        stager.store(smem, tid);
-        __syncthreads();
-        if (blk + 1 < nblocks) stager.load(kb, vb, kv_stride, kbeg + (blk + 1) * kBK, kend, tid);
-
-        const int wbase = kbeg + blk * kBK + 32 * w;   // first key of this wave's slice
-        if (wbase < kend) {
-            const _Float16* Ks = smem;
-            const _Float16* Vt = smem + ST::K_HALVES;
-            f16v S[1];
-            S[0] = qk_subtile<D, ST::KPAD>(Ks, 32 * w, qreg, n, hh);
-            const bool full = wbase + 32 <= kend;
-            const int cnt = full ? 32 : kend - wbase;
-            auto vis = [&](int, int r) { return wbase + key_of(r, hh) < kend; };
-            h2 P[8];
-            const _Float16 alpha = softmax_block<1, false>(S, P, st, c, full, cnt, vis);
-            if (wave_any(alpha != (_Float16)1)) {
-                const float af = (float)alpha;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) acc[dt] *= af;
-            }
-            pv_chunks<D, ST::VPAD, 2>(Vt, 2 * w, P, acc, n, hh);
+    for (int j = 0; j < nsub; ++j) {
+        // sub-tiles j+1 .. j+kSlots-2 stay in flight while j is consumed
+        if (j + kSlots - 1 < nsub) {
+            issue(j + kSlots - 1);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm((kSlots - 1) * NL));
+        } else if (j + 1 < nsub) {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL));
+        } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
-        __syncthreads();
+        const _Float16* Ks = slot_k(j);
+        const _Float16* Vs = Ks + sub_halves<D>();
+        f16v S[1];
+        S[0] = qk_subtile_sw<D>(Ks, 0, qreg, n, hh);
+        const int wbase = kbeg + j * kSub;
+        const bool full = wbase + kSub <= kend;
+        const int cnt = full ? kSub : kend - wbase;
+        h2 P[8];
+        _Float16 alpha;
+        if (full)
+            alpha = softmax_block<1, false>(S, P, st, c, true, kSub, [](int, int) { return true; });
+        else
+            alpha = softmax_block<1, false>(S, P, st, c, false, cnt,
+                                            [&](int, int r) { return key_of(r, hh) < cnt; });
+        if (wave_any(alpha != (_Float16)1)) {
+            const float af = (float)alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= af;
+        }
+        pv_chunks_tr<D, 2>(Vs, 0, P, acc, lane);
     }
 
-    // ---- merge the four wave states (fp32), write this split's partial
-    constexpr int MD = D + 4;                   // padded row stride (bank spread)
-    float* macc = (float*)smem;                 // [4][32][MD]
-    float* mR = macc + 4 * 32 * MD;             // [4][32]
-    float* mL = mR + 4 * 32;                    // [4][32]
+    // ---- this split's normalised partial (fp32)
+    if (row_valid) {
+        const float L = row_sum<false>(st);
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        const int64_t prow = ((int64_t)b * Hq + hq) * nsplit + split;
+        float* orow = o_part + prow * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int d = 32 * dt + 8 * (r >> 2) + 4 * hh + (r & 3);
-            macc[(w * 32 + n) * MD + d] = acc[dt][r];
-        }
-    if (hh == 0) {
-        mR[w * 32 + n] = st.R;
-        mL[w * 32 + n] = row_sum<false>(st);
-    }
-    __syncthreads();
-    const int ngroup_rows = min(32, group - 32 * hc);
-    for (int idx = tid; idx < ngroup_rows * D; idx += kThreads) {
-        const int row = idx / D, d = idx % D;
-        float M = -__builtin_inff();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) M = fmaxf(M, mR[i * 32 + row]);
-        float L = 0.0f, val = 0.0f;
-        if (M != -__builtin_inff()) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float wgt = __builtin_exp2f(mR[i * 32 + row] - M);
-                L += wgt * mL[i * 32 + row];
-                val += wgt * macc[(i * 32 + row) * MD + d];
+            for (int g = 0; g < 4; ++g) {
+                const f4 t = {acc[dt][4 * g + 0] * inv, acc[dt][4 * g + 1] * inv,
+                              acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv};
+                *(f4*)(orow + 32 * dt + 8 * g + 4 * hh) = t;
             }
-        }
-        const int hq_out = hkv * group + 32 * hc + row;
-        const int64_t prow = ((int64_t)b * Hq + hq_out) * nsplit + split;
-        o_part[prow * D + d] = L > 0.0f ? val / L : 0.0f;
-        if (d == 0) lse_part[prow] = L > 0.0f ? (M + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
+        if (hh == 0)
+            lse_part[prow] = L > 0.0f ? (st.R + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
     }
 }
 
@@ -184,14 +183,14 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
-    const int blocks = (a.seqlen_kv + kBK - 1) / kBK;
-    const int per_split = (blocks + a.num_splits - 1) / a.num_splits;
+    const int subs = (a.seqlen_kv + kSub - 1) / kSub;
+    const int per_split = (subs + a.num_splits - 1) / a.num_splits;
     const int head_chunks = (a.gqa_group + 31) / 32;
-    dim3 grid(a.num_splits, (a.num_heads_q / a.gqa_group) * head_chunks, a.batch);
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, stream,
+    const int64_t waves = (int64_t)a.batch * (a.num_heads_q / a.gqa_group) * head_chunks * a.num_splits;
+    hipLaunchKernelGGL(kern, dim3((unsigned)waves), dim3(64), smem, stream,
                        (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
                        a.o_part, a.lse_part, a.seqlen_kv, a.num_heads_q, a.gqa_group,
-                       a.softmax_scale * kLog2e, per_split * kBK, head_chunks);
+                       a.softmax_scale * kLog2e, per_split * kSub, head_chunks, a.num_splits);
     return hipGetLastError();
 }
 

@@ -320,9 +320,14 @@ __device__ __forceinline__ void stage_tile(i32x4 rsrc, uint32_t stride_b, int ro
     }
 }
 
-// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima).  The builtin,
-// unlike an asm statement, also informs the compiler's own wait tracking.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (expcnt and lgkmcnt left at their maxima; vmcnt is split over bits 3:0
+// and 15:14).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// s_waitcnt vmcnt(0).  The builtin, unlike an asm statement, also informs the
+// compiler's own wait tracking.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); }
 
 // A operand of S^T = K Q^T: K row (row0 + sigma(n)), columns 16*kk + 8*hh..+7.
 template <int D>

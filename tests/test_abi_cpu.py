@@ -72,7 +72,8 @@ def test_decode_validation_and_sizes(lib):
     assert ws == ((rows * 128 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
     assert lib.pasa_attn_decode_workspace_bytes(0, 28, 128, 4) == 0
     assert lib.pasa_attn_decode_splits(64, 8192, 28, 7) >= 1
-    assert lib.pasa_attn_decode_splits(1, 100, 1, 1) == 1      # one 128-key block
+    assert lib.pasa_attn_decode_splits(1, 100, 1, 1) == 4      # four 32-key sub-tiles
+    assert lib.pasa_attn_decode_splits(1, 20, 1, 1) == 1
     assert lib.pasa_attn_decode_splits(1, 8192, 28, 3) == 0    # 28 % 3 != 0
 
     def dec(ws_ptr=P, ws_bytes=1 << 30, D=128, n=4, g=7, q=P):

@@ -28,10 +28,173 @@ if ROOT not in sys.path:
 PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16 matrix peak
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E peak
 
-# HBM traffic of the prefill kernel per launch, from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE runs scaled by a copy-kernel calibration; None until measured for
-# the current kernel.
-PREFILL_TRAFFIC_BYTES = None
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "prefill_c2_decode_c5_hbm_traffic.txt")
+CSRC = os.path.join(ROOT, "precision_flashattention_numerics_amd", "csrc")
+
+# Kernel symbols (substrings) of the profiled launches.
+K_PREFILL = "fwd_kernelILi128ELb1ELb0E"      # PASA prefill, head_dim 128, causal
+K_NAIVE = "fwd_kernelILi128ELb1ELb1E"        # naive fp16 prefill, same shape
+K_SPLIT = "decode_split_kernelILi128E"       # decode split, head_dim 128
+K_COMBINE = "decode_combine_kernel"
+
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/trace -o run --output-format csv "
+             "-- python bench.py --steps 20 --warmup 5 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/fetch -o run --output-format csv "
+             "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/write -o run --output-format csv "
+             "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "cfetch": "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/cfetch -o run --output-format csv "
+              "-- python bench.py --calibrate-copy 1024",
+    "cwrite": "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/cwrite -o run --output-format csv "
+              "-- python bench.py --calibrate-copy 1024",
+    "pmc1": "rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU "
+            "SQ_INSTS_VMEM SQ_BUSY_CYCLES SQ_WAVE_CYCLES -d gpurun_out/prof/pmc1 -o run "
+            "--output-format csv -- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "pmc2": "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU "
+            "SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_ACTIVE_INST_ANY SQ_WAIT_ANY GRBM_GUI_ACTIVE "
+            "-d gpurun_out/prof/pmc2 -o run --output-format csv -- python bench.py --steps 3 "
+            "--warmup 1 --no-cpu-baseline",
+}
+
+
+def source_hash():
+    """sha256 over the kernel sources and the ABI header (what the counters describe)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp")))
+    files.append(os.path.join(ROOT, "include", "pasa_attn.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """(prefill_bytes, decode_bytes) per launch from the committed profile summary,
+    or (None, None) if it is missing or was taken on other kernel sources."""
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if "=" in line and not line.startswith("#"):
+                a, b = line.split("=", 1)
+                kv[a.strip()] = b.strip()
+        if kv.get("source_sha256") != source_hash():
+            return None, None
+        return int(kv["prefill_traffic_bytes"]), int(kv["decode_split_traffic_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None, None
+
+
+def _counters(path):
+    """{kernel_substring: {counter: mean value per dispatch}} from a rocprofv3 csv."""
+    import csv
+    import collections
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        acc[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = {}
+    for kname, cs in acc.items():
+        out[kname] = {c: sum(v) / len(v) for c, v in cs.items()}
+    return out
+
+
+def _pick(table, sub):
+    for k, v in table.items():
+        if sub in k:
+            return v
+    raise KeyError(sub)
+
+
+def summarize_profile(d):
+    """Write the text summaries under profiles/ from a rocprofv3 output directory
+    laid out as PROFILE_CMDS produce it."""
+    import csv
+    import workloads as W
+    os.makedirs(PROFILES, exist_ok=True)
+    wp, wd = W.CONFIGS["c2"], W.CONFIGS["c5"]
+    stats = {r["Name"]: r for r in csv.DictReader(open(os.path.join(d, "trace", "run_kernel_stats.csv")))}
+
+    def st(sub):
+        for k, v in stats.items():
+            if sub in k:
+                return v
+        raise KeyError(sub)
+    lines = ["# rocprofv3 kernel trace of bench.py: PASA prefill on the Qwen2-7B-shaped causal workload",
+             "# (batch 1, seq 4096, 28 query / 4 kv heads, head_dim 128) and split-KV decode on the decode",
+             "# workload (batch 64, kv length 8192, 28/4 heads, head_dim 128), one MI355X.",
+             "# command: " + PROFILE_CMDS["trace"],
+             f"# kernel sources sha256: {source_hash()}",
+             "kernel                         calls  avg_us    min_us    max_us   algorithmic    rate"]
+    pre = st(K_PREFILL)
+    avg_p = float(pre["AverageNs"]) * 1e-3
+    lines.append(f"pasa prefill (c2)            {int(pre['Calls']):6d} {avg_p:8.2f} "
+                 f"{float(pre['MinNs'])*1e-3:8.2f} {float(pre['MaxNs'])*1e-3:8.2f}  "
+                 f"{wp.flops():.4e} flop  {wp.flops()/avg_p/1e6:8.1f} TFLOP/s "
+                 f"({wp.flops()/avg_p/1e6/PEAK_FP16_TFLOPS:.3f} of 2500)")
+    sp = st(K_SPLIT)
+    avg_s = float(sp["AverageNs"]) * 1e-3
+    cb = st(K_COMBINE)
+    avg_c = float(cb["AverageNs"]) * 1e-3
+    lines.append(f"pasa decode split (c5)       {int(sp['Calls']):6d} {avg_s:8.2f} "
+                 f"{float(sp['MinNs'])*1e-3:8.2f} {float(sp['MaxNs'])*1e-3:8.2f}  "
+                 f"{wd.io_bytes():.4e} B     {wd.io_bytes()/avg_s/1e3:8.1f} GB/s "
+                 f"({wd.io_bytes()/avg_s/1e3/PEAK_HBM_GBPS:.3f} of 8000)")
+    lines.append(f"pasa decode combine (c5)     {int(cb['Calls']):6d} {avg_c:8.2f} "
+                 f"{float(cb['MinNs'])*1e-3:8.2f} {float(cb['MaxNs'])*1e-3:8.2f}")
+    try:
+        nv = st(K_NAIVE)
+        lines.append(f"naive fp16 prefill (c2)      {int(nv['Calls']):6d} {float(nv['AverageNs'])*1e-3:8.2f}")
+    except KeyError:
+        pass
+    open(os.path.join(PROFILES, "prefill_c2_decode_c5_kernel_trace.txt"), "w").write("\n".join(lines) + "\n")
+
+    fetch = _counters(os.path.join(d, "fetch", "run_counter_collection.csv"))
+    write = _counters(os.path.join(d, "write", "run_counter_collection.csv"))
+    cfetch = _counters(os.path.join(d, "cfetch", "run_counter_collection.csv"))
+    cwrite = _counters(os.path.join(d, "cwrite", "run_counter_collection.csv"))
+    copy_bytes = 1024 * (1 << 20)
+    cf = _pick(cfetch, "copyBuffer")["FETCH_SIZE"] * 1024
+    cw = _pick(cwrite, "copyBuffer")["WRITE_SIZE"] * 1024
+    ff, wf = copy_bytes / cf, copy_bytes / cw
+    pf = _pick(fetch, K_PREFILL)["FETCH_SIZE"]
+    pw = _pick(write, K_PREFILL)["WRITE_SIZE"]
+    sf = _pick(fetch, K_SPLIT)["FETCH_SIZE"]
+    sw = _pick(write, K_SPLIT)["WRITE_SIZE"]
+    p_bytes = int(pf * 1024 * ff + pw * 1024 * wf)
+    s_bytes = int(sf * 1024 * ff + sw * 1024 * wf)
+    t = ["# HBM traffic per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),",
+         "# each scaled by what the same counter reads for a plain 1 GiB device-to-device copy.",
+         "# commands:",
+         "#   " + PROFILE_CMDS["fetch"], "#   " + PROFILE_CMDS["write"],
+         "#   " + PROFILE_CMDS["cfetch"], "#   " + PROFILE_CMDS["cwrite"],
+         f"source_sha256={source_hash()}",
+         f"copy_bytes={copy_bytes}",
+         f"copy_fetch_kib={cf/1024:.1f}", f"copy_write_kib={cw/1024:.1f}",
+         f"fetch_factor={ff:.4f}", f"write_factor={wf:.4f}",
+         f"prefill_fetch_kib={pf:.1f}", f"prefill_write_kib={pw:.1f}",
+         f"prefill_traffic_bytes={p_bytes}",
+         f"prefill_algorithmic_bytes={wp.io_bytes()}",
+         f"decode_split_fetch_kib={sf:.1f}", f"decode_split_write_kib={sw:.1f}",
+         f"decode_split_traffic_bytes={s_bytes}",
+         f"decode_algorithmic_bytes={wd.io_bytes()}"]
+    open(TRAFFIC_FILE, "w").write("\n".join(t) + "\n")
+
+    rows = []
+    for key, title in (("pmc1", "instruction counts"), ("pmc2", "busy / wait cycles")):
+        path = os.path.join(d, key, "run_counter_collection.csv")
+        if not os.path.exists(path):
+            continue
+        c = _counters(path)
+        rows.append(f"# {title}: " + PROFILE_CMDS[key])
+        for name, sub in (("pasa prefill (c2)", K_PREFILL), ("pasa decode split (c5)", K_SPLIT)):
+            vals = _pick(c, sub)
+            rows.append(f"{name}: " + ", ".join(f"{k}={v:.0f}" for k, v in sorted(vals.items())))
+    if rows:
+        open(os.path.join(PROFILES, "prefill_c2_decode_c5_counters.txt"), "w").write("\n".join(rows) + "\n")
+    print("\n".join(lines + t))
 
 
 def parse():
@@ -43,6 +206,10 @@ def parse():
                     help="skip the oracle timing and the sampled parity check")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--summarize-profile", metavar="DIR", default=None,
+                    help="write the text summaries under profiles/ from a rocprofv3 output "
+                         "directory (subdirectories trace, fetch, write, cfetch, cwrite, pmc1, "
+                         "pmc2 made by the commands recorded in those summaries), then exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times "
                          "(reference for the HBM byte counters), then exit")
@@ -69,6 +236,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
         return
 
     import numpy as np
@@ -127,6 +297,7 @@ def main():
     dec_avg = sum(dec_ms) / K
     log(f"timed {K} steps: prefill {pre_avg:.4f} ms, decode {dec_avg:.4f} ms, wall {wall:.3f} s")
 
+    traffic_p, traffic_d = recorded_traffic()
     flops = wp.flops()
     tflops = flops / (pre_avg * 1e-3) / 1e12
     dec_bytes = wd.io_bytes()
@@ -200,10 +371,10 @@ def main():
         "decode_GBps": round(dec_gbps, 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
-                     "traffic": PREFILL_TRAFFIC_BYTES},
+                     "traffic": traffic_p},
         "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps, 1),
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                            "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+                            "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic_d},
         "cpu_baseline": cpu,
         **out,
     }

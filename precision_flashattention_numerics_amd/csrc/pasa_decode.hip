@@ -180,9 +180,7 @@ template <int D>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
     auto kern = decode_split_kernel<D>;
     constexpr int smem = dec_smem_bytes<D>();
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return e;
+    static_assert(smem <= 64 * 1024, "dynamic LDS above 64 KB would need an opt-in");
     const int subs = (a.seqlen_kv + kSub - 1) / kSub;
     const int per_split = (subs + a.num_splits - 1) / a.num_splits;
     const int head_chunks = (a.gqa_group + 31) / 32;

@@ -214,3 +214,43 @@ def test_error_writes_nothing(pasa):
     torch.cuda.synchronize()
     assert rc == -2
     assert bool((o == 7.0).all())
+
+
+# ----------------------------------------------------------------- limits
+@pytest.mark.parametrize("causal", [False, True])
+def test_max_kv_length_flat_rows(pasa, causal):
+    """seqlen_kv = 65504, the most keys the fp16 running sum may hold: with
+    q = 0 every weight is 1, so the running sum reaches 65504 exactly and O is
+    the mean of the visible values."""
+    import torch
+    Skv, Sq, D = 65504, 5, 128
+    w = W.custom(1, Sq, Skv, 2, 1, D, causal, kind="normal", seed=65504)
+    q, k, v = W.generate(w)
+    q[:] = 0
+    tq, tk, tv = to_gpu(q, k, v)
+    o, lse = pasa.attn_fwd(tq, tk, tv, causal=causal, scale=w.scale)
+    torch.cuda.synchronize()
+    ro, rl = attn_fp64(q, k, v, w.scale, causal)
+    o = o.cpu().numpy()
+    err = rel_rmse(o, ro)
+    say("flat 65504 rel_rmse", err)
+    assert nonfinite(o) == 0
+    assert err <= REL_RMSE_MAX
+    assert lse_ok(lse.cpu().numpy(), rl)
+
+
+def test_decode_deterministic_and_matches_prefill_shape(pasa):
+    """The decode path twice gives identical bits; it agrees with the prefill
+    kernel run on the same single-token queries."""
+    import torch
+    w = W.custom(4, 1, 3000, 14, 2, 128, False, kind="bias", seed=14, bias=30.0)
+    q, k, v = W.generate(w)
+    tq, tk, tv = to_gpu(q, k, v)
+    o1, l1 = pasa.attn_decode(tq, tk, tv, num_splits=5, scale=w.scale)
+    o2, l2 = pasa.attn_decode(tq, tk, tv, num_splits=5, scale=w.scale)
+    op, lp = pasa.attn_fwd(tq, tk, tv, causal=False, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    a, b = o1.cpu().numpy(), op.cpu().numpy()
+    assert rel_rmse(a, b) <= 2 * REL_RMSE_MAX
+    assert np.max(np.abs(l1.cpu().numpy() - lp.cpu().numpy()[:, :, 0])) <= 1e-2

@@ -163,9 +163,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = (f16v){};
     f16v S[2];
-    h2 P[16];
+    h2 P[16];              // exponent arguments X of a block, then its P in place
+    _Float16 apend = 1;    // alpha of the block whose X is held in P
 
-    // matrix phase of block j: P V for block j-1, then S^T = K Q^T for block j
+    // matrix phase of block j: S^T = K Q^T for block j with the exponentials
+    // and row sums of block j-1 issued between the products, then P V for
+    // block j-1, as one straight-line region whose LDS operand reads are kept
+    // several products ahead of their use
     auto mphase = [&](int j) {
         __builtin_amdgcn_s_setprio(1);
         const bool pv = j >= 1 && active(j - 1);
@@ -173,24 +177,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const _Float16* Vs = Vst + ((j - 1) & 1) * tile_halves<D>();
         const _Float16* Ks = Kst + (j & 1) * tile_halves<D>();
         if (pv && qk) {
-            // one straight-line region of 2 * (16 * D / 64) products whose LDS
-            // operand reads are kept several products ahead of their use
-            pv_chunks_tr<D, 4>(Vs, 0, P, acc, lane);
             S[0] = qk_subtile_sw<D>(Ks, 0, qreg, n, hh);
             S[1] = qk_subtile_sw<D>(Ks, 32, qreg, n, hh);
-            constexpr int NMF = 2 * 4 * (D / 32) + 2 * (D / 16);   // products in the region
-            constexpr int NRD = 2 * 4 * (D / 32) + 2 * (D / 16);   // 2 reads per PV product, 1 per QK
+            softmax_exp<2, NAIVE>(P, st, apend);
+            pv_chunks_tr<D, 4>(Vs, 0, P, acc, lane);
+            constexpr int NQK = 2 * (D / 16);   // one K read each
+            constexpr int NPV = 4 * (D / 32);   // two V reads each
             constexpr int AHEAD = 8;
-            constexpr int STEADY = (NRD - AHEAD) / 2;
             __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
-            for (int i = 0; i < STEADY; ++i) {
+            for (int i = 0; i < NQK; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, NMF - STEADY, 0);
+#pragma unroll
+            for (int i = 0; i < NPV; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (2 * i + AHEAD < 2 * NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
         } else {
-            if (pv) pv_chunks_tr<D, 4>(Vs, 0, P, acc, lane);
+            if (pv) {
+                softmax_exp<2, NAIVE>(P, st, apend);
+                pv_chunks_tr<D, 4>(Vs, 0, P, acc, lane);
+            }
             if (qk) {
                 S[0] = qk_subtile_sw<D>(Ks, 0, qreg, n, hh);
                 S[1] = qk_subtile_sw<D>(Ks, 32, qreg, n, hh);
@@ -198,21 +207,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         __builtin_amdgcn_s_setprio(0);
     };
-    // vector phase of block j: half-precision softmax, accumulator rescale
+    // vector phase of block j: the shift, the fp16 tile and its exponent
+    // arguments; the accumulator rescale the new running maximum calls for
     auto vphase = [&](int j) {
         if (!active(j)) return;
         const int kbase = j * kBC;
-        _Float16 alpha;
+        _Float16 d;
         if (kbase + kBC <= wave_lim_lo) {   // the whole block is visible to the wave
-            alpha = softmax_block<2, NAIVE>(S, P, st, c, true, kBC, [](int, int) { return true; });
+            d = softmax_tile<2, NAIVE>(S, P, st, c, true, kBC, [](int, int) { return true; });
         } else {
             const int m = lim - kbase;        // keys [0, m) of the block are visible
             const int cnt = max(0, min(kBC, m));
-            alpha = softmax_block<2, NAIVE>(S, P, st, c, false, cnt,
-                                            [&](int t, int r) { return 32 * t + key_of(r, hh) < m; });
+            d = softmax_tile<2, NAIVE>(S, P, st, c, false, cnt,
+                                       [&](int t, int r) { return 32 * t + key_of(r, hh) < m; });
         }
-        if (wave_any(alpha != (_Float16)1)) {
-            const float af = (float)alpha;
+        apend = hexp2(d);
+        if (wave_any(apend != (_Float16)1)) {
+            const float af = (float)apend;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) acc[dt] *= af;
         }

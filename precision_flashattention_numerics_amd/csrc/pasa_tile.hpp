@@ -69,14 +69,21 @@ struct RowState {
 };
 
 // One key block of NT 32-key sub-tiles for the row held by this lane (and by
-// the lane 32 apart, which holds the other half of the row's keys).
+// the lane 32 apart, which holds the other half of the row's keys), in two
+// steps that a kernel may run at different times:
+//   softmax_tile  the shift, the fp16 tile T and the exponent arguments
+//                 X = T - s; updates the running maximum and returns
+//                 d = fp16(R - R') (0 when the row sees no key of the block)
+//   softmax_exp   P = exp2(X) in place, the row sum r, and the running sum
+//                 rescaled by alpha = exp2(d), the factor the caller also
+//                 applies to its accumulator
+// Arguments:
 //   S       fp32 scores (unscaled q.k), register r of sub-tile t is key
 //           32*t + key_of(r, hh) of the block
+//   X / P   packed fp16 pairs, X[8*t + r/2] = keys r, r+1 of sub-tile t
 //   full    every key of the block is visible to every row of the wave
 //   cnt     number of keys of the block visible to this row
 //   vis     vis(t, r) -> visibility of that key (used only when !full)
-// Writes P (packed fp16 pairs, P[8*t + r/2] = keys r, r+1 of sub-tile t) and
-// returns alpha, the factor the caller applies to its accumulator.
 //
 // The tile maximum m_b = max_j fp16(c*S_j - off) equals fp16(c*max_j S_j - off)
 // because rounding to fp16 is monotone; it is therefore taken from one fp32
@@ -84,10 +91,9 @@ struct RowState {
 // (m_b > THETA -> centre at the row maximum) is made before the fp16 tile is
 // formed, so the tile is formed exactly once and without a branch.
 template <int NT, bool NAIVE, typename Vis>
-__device__ __forceinline__ _Float16 softmax_block(const f16v (&S)[NT], h2 (&P)[8 * NT],
-                                                  RowState& st, float c, bool full, int cnt,
-                                                  Vis vis) {
-    h2 T[8 * NT];
+__device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 * NT],
+                                                 RowState& st, float c, bool full, int cnt,
+                                                 Vis vis) {
     _Float16 mb;
     float off = 0.0f;
     if (!NAIVE) {
@@ -123,7 +129,7 @@ __device__ __forceinline__ _Float16 softmax_block(const f16v (&S)[NT], h2 (&P)[8
                     if (!vis(t, r)) x.x = kHalfNegInf;
                     if (!vis(t, r + 1)) x.y = kHalfNegInf;
                 }
-                T[8 * t + r / 2] = x;
+                X[8 * t + r / 2] = x;
             }
     } else {
         const _Float16 ch = (_Float16)c;
@@ -137,7 +143,7 @@ __device__ __forceinline__ _Float16 softmax_block(const f16v (&S)[NT], h2 (&P)[8
                     if (!vis(t, r)) x.x = kHalfNegInf;
                     if (!vis(t, r + 1)) x.y = kHalfNegInf;
                 }
-                T[8 * t + r / 2] = x;
+                X[8 * t + r / 2] = x;
                 mm = hmax(mm, x);
             }
         mb = xmax32(mm.x > mm.y ? mm.x : mm.y);
@@ -147,9 +153,16 @@ __device__ __forceinline__ _Float16 softmax_block(const f16v (&S)[NT], h2 (&P)[8
     const _Float16 s = cnt > 0 ? (_Float16)(Rn - off) : (_Float16)0;
     const h2 s2 = {s, s};
 #pragma unroll
-    for (int i = 0; i < 8 * NT; ++i) T[i] = T[i] - s2;
+    for (int i = 0; i < 8 * NT; ++i) X[i] = X[i] - s2;
+    const _Float16 d = cnt > 0 ? (_Float16)(st.R - Rn) : (_Float16)0;
+    st.R = Rn;
+    return d;
+}
+
+template <int NT, bool NAIVE>
+__device__ __forceinline__ void softmax_exp(h2 (&P)[8 * NT], RowState& st, _Float16 alpha) {
 #pragma unroll
-    for (int i = 0; i < 8 * NT; i += 4) hexp2_pk4(T + i, P + i);
+    for (int i = 0; i < 8 * NT; i += 4) hexp2_pk4(P + i, P + i);
 
     // fp16 pairwise tree sum of the lane's exponentials, then across halves
     h2 a[4 * NT];
@@ -161,12 +174,19 @@ __device__ __forceinline__ _Float16 softmax_block(const f16v (&S)[NT], h2 (&P)[8
         for (int i = 0; i < w; ++i) a[i] = a[2 * i] + a[2 * i + 1];
     const _Float16 rsum = xsum32((_Float16)(a[0].x + a[0].y));
 
-    const _Float16 alpha = cnt > 0 ? hexp2((_Float16)(st.R - Rn)) : (_Float16)1;
     if (!NAIVE)
         comp_add(st.lhi, st.llo, alpha, rsum);
     else
         st.lsum = (float)alpha * st.lsum + (float)rsum;
-    st.R = Rn;
+}
+
+// Both steps back to back.
+template <int NT, bool NAIVE, typename Vis>
+__device__ __forceinline__ _Float16 softmax_block(const f16v (&S)[NT], h2 (&P)[8 * NT],
+                                                  RowState& st, float c, bool full, int cnt,
+                                                  Vis vis) {
+    const _Float16 alpha = hexp2(softmax_tile<NT, NAIVE>(S, P, st, c, full, cnt, vis));
+    softmax_exp<NT, NAIVE>(P, st, alpha);
     return alpha;
 }
 

@@ -312,6 +312,18 @@ def main():
     on, _ = pasa.naive_attn_fwd(tqp, tkp, tvp, causal=wp.causal, scale=wp.scale)
     torch.cuda.synchronize()
     out["naive_nonfinite"] = nonfinite(on.cpu().numpy())
+    # the variant with fp16 running maximum and offset: its error is reported
+    # beside the default's (and its speed, outside the timed steps)
+    os_, ls_ = pasa.attn_fwd_strict(tqp, tkp, tvp, causal=wp.causal, scale=wp.scale)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        pasa.attn_fwd_strict(tqp, tkp, tvp, causal=wp.causal, scale=wp.scale, out=os_, lse=ls_)
+    e1.record()
+    torch.cuda.synchronize()
+    out["strict_tflops"] = round(flops / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e12, 3)
+    os_np, ls_np = os_.cpu().numpy(), ls_.cpu().numpy()
+    out["strict_nonfinite"] = nonfinite(os_np)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -339,6 +351,8 @@ def main():
         h, i = np.divmod(rem, wp.seqlen_q)
         out["rel_rmse_sampled"] = rel_rmse(o_np[b, i, h], ro)
         out["lse_max_abs_err_sampled"] = float(np.max(np.abs(l_np[b, h, i] - rl)))
+        out["strict_rel_rmse_sampled"] = rel_rmse(os_np[b, i, h], ro)
+        out["strict_lse_max_abs_err_sampled"] = float(np.max(np.abs(ls_np[b, h, i] - rl)))
         cpu = {"value": cpu_flops / tc / 1e12, "unit": "TFLOP/s", "cores": num_threads(),
                "kind": "oracle",
                "sample": f"{n_rows} random query rows of the prefill workload "

@@ -71,6 +71,23 @@ int pasa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* l
                   int head_dim, float softmax_scale, int causal, hipStream_t stream);
 
 /*
+ * PASA forward with all of the per-row bookkeeping in fp16 ("Online
+ * Pseudo-average Shifting Attention (PASA) ...", Abstract: the Flash-Attention
+ * process runs in half precision throughout).  pasa_attn_fwd keeps the
+ * running maximum R and the block offset in fp32 and everything tile-shaped
+ * (scores, exponentials, block maxima and sums, rescale factors) plus the
+ * running sum in fp16; this variant also rounds R and the offset to fp16 where
+ * they are formed.  It is exposed so that its error can be measured beside the
+ * default.  Usable while |softmax_scale * q.k| * log2(e) stays below about
+ * 3.2e4: beyond that the fp16 rounding of R (a step of 16 there) lets the
+ * exponentials of a block exceed 1 by up to 2^8 and the fp16 running sum can
+ * overflow.  Arguments, layouts and errors as pasa_attn_fwd.
+ */
+int pasa_attn_fwd_strict(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group,
+                         int head_dim, float softmax_scale, int causal, hipStream_t stream);
+
+/*
  * Naive fp16 Flash-Attention forward: the same blockwise kernel WITHOUT the
  * pseudo-average shift.  The unscaled score tile QK^T is rounded to fp16 and
  * then multiplied by the scale in fp16, as a plain half-precision Flash

@@ -29,6 +29,8 @@ _lib.pasa_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, 
 _lib.pasa_attn_fwd.restype = _i
 _lib.pasa_naive_attn_fwd.argtypes = _lib.pasa_attn_fwd.argtypes
 _lib.pasa_naive_attn_fwd.restype = _i
+_lib.pasa_attn_fwd_strict.argtypes = _lib.pasa_attn_fwd.argtypes
+_lib.pasa_attn_fwd_strict.restype = _i
 _lib.pasa_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
 _lib.pasa_attn_decode.restype = _i
 _lib.pasa_attn_decode_splits.argtypes = [_i, _i, _i, _i]
@@ -113,6 +115,13 @@ def attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, return_lse=T
     """PASA forward. q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] fp16 -> (o, lse)."""
     return _fwd(_lib.pasa_attn_fwd, "pasa_attn_fwd", q, k, v, causal, scale, out, lse,
                 return_lse, stream)
+
+
+def attn_fwd_strict(q, k, v, causal=False, scale=None, out=None, lse=None, return_lse=True,
+                    stream=None):
+    """PASA forward with fp16 running maximum and offset as well; same interface."""
+    return _fwd(_lib.pasa_attn_fwd_strict, "pasa_attn_fwd_strict", q, k, v, causal, scale, out,
+                lse, return_lse, stream)
 
 
 def naive_attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, return_lse=True,

@@ -28,7 +28,10 @@ struct DecodeArgs {
     int num_splits;
 };
 
-hipError_t launch_fwd(const FwdArgs& a, bool naive, hipStream_t stream);
+// Forward variants: PASA, PASA with fp16 running maximum and offset, and the
+// naive fp16 Flash-Attention overflow exhibit.
+enum { kVarPasa = 0, kVarStrict = 1, kVarNaive = 2 };
+hipError_t launch_fwd(const FwdArgs& a, int variant, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_combine(const float* o_part, const float* lse_part, void* o, float* lse,
                                  int batch, int num_heads_q, int head_dim, int num_splits,

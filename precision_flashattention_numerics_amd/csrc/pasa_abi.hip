@@ -38,7 +38,7 @@ int check_common(const void* q, const void* k, const void* v, const void* o, int
     return PASA_OK;
 }
 
-int fwd_common(bool naive, const void* q, const void* k, const void* v, void* o, float* lse,
+int fwd_common(int variant, const void* q, const void* k, const void* v, void* o, float* lse,
                int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group,
                int head_dim, float softmax_scale, int causal, hipStream_t stream) {
     int rc = check_common(q, k, v, o, batch, seqlen_q, seqlen_kv, num_heads_q, gqa_group,
@@ -48,7 +48,7 @@ int fwd_common(bool naive, const void* q, const void* k, const void* v, void* o,
     if (seqlen_kv > kMaxFp16Sum) return PASA_ERR_UNSUPPORTED;
     pasa::FwdArgs a{q, k, v, o, lse, batch, seqlen_q, seqlen_kv, num_heads_q, gqa_group,
                     head_dim, softmax_scale, causal};
-    return pasa::launch_fwd(a, naive, stream) == hipSuccess ? PASA_OK : PASA_ERR_HIP;
+    return pasa::launch_fwd(a, variant, stream) == hipSuccess ? PASA_OK : PASA_ERR_HIP;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -60,15 +60,22 @@ extern "C" {
 int pasa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
                   int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group, int head_dim,
                   float softmax_scale, int causal, hipStream_t stream) {
-    return fwd_common(false, q, k, v, o, lse, batch, seqlen_q, seqlen_kv, num_heads_q, gqa_group,
-                      head_dim, softmax_scale, causal, stream);
+    return fwd_common(pasa::kVarPasa, q, k, v, o, lse, batch, seqlen_q, seqlen_kv, num_heads_q,
+                      gqa_group, head_dim, softmax_scale, causal, stream);
+}
+
+int pasa_attn_fwd_strict(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group,
+                         int head_dim, float softmax_scale, int causal, hipStream_t stream) {
+    return fwd_common(pasa::kVarStrict, q, k, v, o, lse, batch, seqlen_q, seqlen_kv, num_heads_q,
+                      gqa_group, head_dim, softmax_scale, causal, stream);
 }
 
 int pasa_naive_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                         int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group,
                         int head_dim, float softmax_scale, int causal, hipStream_t stream) {
-    return fwd_common(true, q, k, v, o, lse, batch, seqlen_q, seqlen_kv, num_heads_q, gqa_group,
-                      head_dim, softmax_scale, causal, stream);
+    return fwd_common(pasa::kVarNaive, q, k, v, o, lse, batch, seqlen_q, seqlen_kv, num_heads_q,
+                      gqa_group, head_dim, softmax_scale, causal, stream);
 }
 
 int pasa_attn_decode_splits(int batch, int seqlen_kv, int num_heads_q, int gqa_group) {

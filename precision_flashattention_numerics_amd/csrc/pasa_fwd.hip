@@ -88,11 +88,13 @@ __device__ __forceinline__ Item decode_item(int L, int N, int B, int Hq, int g, 
     return it;
 }
 
-template <int D, bool CAUSAL, bool NAIVE>
+template <int D, bool CAUSAL, int VAR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, _Float16* __restrict__ o, float* __restrict__ lse,
     int B, int Sq, int Skv, int Hq, int group, float c, int n_qtiles) {
+    constexpr bool NAIVE = VAR == kVarNaive;
+    constexpr bool STRICT = VAR == kVarStrict;
     constexpr int KK = D / 16;
     constexpr int DT = D / 32;
     extern __shared__ __attribute__((aligned(1024))) _Float16 smem[];
@@ -214,12 +216,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int kbase = j * kBC;
         _Float16 d;
         if (kbase + kBC <= wave_lim_lo) {   // the whole block is visible to the wave
-            d = softmax_tile<2, NAIVE>(S, P, st, c, true, kBC, [](int, int) { return true; });
+            auto all = [](int, int) { return true; };
+            d = softmax_tile<2, NAIVE, decltype(all), STRICT>(S, P, st, c, true, kBC, all);
         } else {
             const int m = lim - kbase;        // keys [0, m) of the block are visible
             const int cnt = max(0, min(kBC, m));
-            d = softmax_tile<2, NAIVE>(S, P, st, c, false, cnt,
-                                       [&](int t, int r) { return 32 * t + key_of(r, hh) < m; });
+            auto vis = [&](int t, int r) { return 32 * t + key_of(r, hh) < m; };
+            d = softmax_tile<2, NAIVE, decltype(vis), STRICT>(S, P, st, c, false, cnt, vis);
         }
         apend = hexp2(d);
         if (wave_any(apend != (_Float16)1)) {
@@ -270,9 +273,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
 }
 
-template <int D, bool CAUSAL, bool NAIVE>
+template <int D, bool CAUSAL, int VAR>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
-    auto kern = fwd_kernel<D, CAUSAL, NAIVE>;
+    auto kern = fwd_kernel<D, CAUSAL, VAR>;
     constexpr int smem = fwd_smem_bytes<D>();
     static_assert(smem <= 64 * 1024, "dynamic LDS above 64 KB would need an opt-in");
     const int n_qtiles = (a.seqlen_q + kBR - 1) / kBR;
@@ -284,17 +287,19 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_var(const FwdArgs& a, int variant, hipStream_t stream) {
+    if (variant == kVarNaive)
+        return a.causal ? launch_one<D, true, kVarNaive>(a, stream) : launch_one<D, false, kVarNaive>(a, stream);
+    if (variant == kVarStrict)
+        return a.causal ? launch_one<D, true, kVarStrict>(a, stream) : launch_one<D, false, kVarStrict>(a, stream);
+    return a.causal ? launch_one<D, true, kVarPasa>(a, stream) : launch_one<D, false, kVarPasa>(a, stream);
+}
+
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs& a, bool naive, hipStream_t stream) {
-    if (a.head_dim == 128) {
-        if (naive)
-            return a.causal ? launch_one<128, true, true>(a, stream) : launch_one<128, false, true>(a, stream);
-        return a.causal ? launch_one<128, true, false>(a, stream) : launch_one<128, false, false>(a, stream);
-    }
-    if (naive)
-        return a.causal ? launch_one<64, true, true>(a, stream) : launch_one<64, false, true>(a, stream);
-    return a.causal ? launch_one<64, true, false>(a, stream) : launch_one<64, false, false>(a, stream);
+hipError_t launch_fwd(const FwdArgs& a, int variant, hipStream_t stream) {
+    return a.head_dim == 128 ? launch_var<128>(a, variant, stream) : launch_var<64>(a, variant, stream);
 }
 
 }  // namespace pasa

@@ -90,10 +90,18 @@ struct RowState {
 // max pass that runs beside the pseudo-average sum, and the refine decision
 // (m_b > THETA -> centre at the row maximum) is made before the fp16 tile is
 // formed, so the tile is formed exactly once and without a branch.
-template <int NT, bool NAIVE, typename Vis>
+//
+// STRICT (PASA only) also holds the running maximum R and the offset off in
+// fp16: each is rounded to fp16 where it is formed, and R' = max(R, off + m_b)
+// is an fp16 addition.  This is usable while |c * score| stays well inside
+// the fp16 range (about 3.2e4): the rounding of R (ulp 16 there) moves the
+// largest P of a block up to 2^8 above 1.
+template <int NT, bool NAIVE, typename Vis, bool STRICT = false>
 __device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 * NT],
                                                  RowState& st, float c, bool full, int cnt,
                                                  Vis vis) {
+    static_assert(!(STRICT && NAIVE), "the strict variant is a PASA variant");
+    auto r16 = [](float x) { return STRICT ? (float)(_Float16)x : x; };
     _Float16 mb;
     float off = 0.0f;
     if (!NAIVE) {
@@ -110,13 +118,13 @@ __device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 
             }
         const float sum = xsum32((ps[0] + ps[1]) + (ps[2] + ps[3]));
         const float m32 = xmax32(fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3])));
-        const float cmu = cnt > 0 ? c * (sum / (float)cnt) : st.R;
+        const float cmu = cnt > 0 ? r16(c * (sum / (float)cnt)) : st.R;
         off = (st.R == -__builtin_inff()) ? cmu : fmaxf(cmu, st.R);
         mb = fma_to_h(m32, c, -off);
         // refine: the tile's largest entries would sit where fp16 is coarse
         // (or overflow); centre the row at its own maximum instead
         if (cnt > 0 && !(mb <= (_Float16)kTheta)) {
-            off = c * m32;
+            off = r16(c * m32);
             mb = fma_to_h(m32, c, -off);
         }
         const float noff = -off;
@@ -149,7 +157,8 @@ __device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 
         mb = xmax32(mm.x > mm.y ? mm.x : mm.y);
     }
 
-    const float Rn = cnt > 0 ? fmaxf(st.R, off + (float)mb) : st.R;
+    const float top = STRICT ? (float)((_Float16)off + mb) : off + (float)mb;
+    const float Rn = cnt > 0 ? fmaxf(st.R, top) : st.R;
     const _Float16 s = cnt > 0 ? (_Float16)(Rn - off) : (_Float16)0;
     const h2 s2 = {s, s};
 #pragma unroll

@@ -28,7 +28,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared()
-    for fn in ("pasa_attn_fwd", "pasa_naive_attn_fwd", "pasa_attn_decode",
+    for fn in ("pasa_attn_fwd", "pasa_attn_fwd_strict", "pasa_naive_attn_fwd", "pasa_attn_decode",
                "pasa_attn_decode_combine", "pasa_attn_decode_workspace_bytes",
                "pasa_attn_decode_splits", "pasa_status_string"):
         assert fn in names
@@ -48,7 +48,7 @@ def _fwd(lib, name, q=P, k=P, v=P, o=P, B=1, Sq=8, Skv=8, Hq=2, g=1, D=64, scale
     return f(q, k, v, o, None, B, Sq, Skv, Hq, g, D, ctypes.c_float(scale), causal, None)
 
 
-@pytest.mark.parametrize("name", ["pasa_attn_fwd", "pasa_naive_attn_fwd"])
+@pytest.mark.parametrize("name", ["pasa_attn_fwd", "pasa_attn_fwd_strict", "pasa_naive_attn_fwd"])
 def test_fwd_validation(lib, name):
     assert _fwd(lib, name, q=None) == -1
     assert _fwd(lib, name, o=None) == -1

@@ -19,11 +19,11 @@ def pasa():
     return p
 
 
-def run_fwd(pasa, w, naive=False):
+def run_fwd(pasa, w, naive=False, strict=False):
     import torch
     q, k, v = W.generate(w)
     tq, tk, tv = to_gpu(q, k, v)
-    fn = pasa.naive_attn_fwd if naive else pasa.attn_fwd
+    fn = pasa.naive_attn_fwd if naive else pasa.attn_fwd_strict if strict else pasa.attn_fwd
     o, lse = fn(tq, tk, tv, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
     return (q, k, v), o.cpu().numpy(), lse.cpu().numpy()
@@ -66,6 +66,37 @@ def test_config_full_vs_oracle(pasa, name):
     err = rel_rmse(o, ro)
     say(name, "rel_rmse", err, "nonfinite", n_bad, "lse_err", lse_error(lse, rl)[:2])
     assert n_bad == 0
+    assert err <= REL_RMSE_MAX
+    assert lse_ok(lse, rl)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_strict_config_full_vs_oracle(pasa, name):
+    """fp16 running maximum and offset as well: same bar (every config keeps
+    |c * score| well below 3.2e4)."""
+    w = W.CONFIGS[name]
+    say("strict config", name)
+    (q, k, v), o, lse = run_fwd(pasa, w, strict=True)
+    ro, rl = attn_fp64(q, k, v, w.scale, w.causal)
+    n_bad = nonfinite(o) + nonfinite(lse)
+    err = rel_rmse(o, ro)
+    say(name, "strict rel_rmse", err, "nonfinite", n_bad, "lse_err", lse_error(lse, rl)[:2])
+    assert n_bad == 0
+    assert err <= REL_RMSE_MAX
+    assert lse_ok(lse, rl)
+
+
+@pytest.mark.parametrize("shape", [s for s in SMALL if s[0] * s[1] * s[3] <= 600 and s[2] >= 64],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_strict_small_shapes_vs_oracle(pasa, shape):
+    B, Sq, Skv, Hq, Hkv, D, causal = shape
+    w = W.custom(B, Sq, Skv, Hq, Hkv, D, causal, kind="bias", seed=sum(shape) + 7, bias=10.0)
+    say("strict case", shape)
+    (q, k, v), o, lse = run_fwd(pasa, w, strict=True)
+    ro, rl = attn_fp64(q, k, v, w.scale, causal)
+    assert nonfinite(o) == 0
+    err = rel_rmse(o, ro)
+    say("rel_rmse", err)
     assert err <= REL_RMSE_MAX
     assert lse_ok(lse, rl)
 

@@ -33,29 +33,30 @@ TRAFFIC_FILE = os.path.join(PROFILES, "prefill_c2_decode_c5_hbm_traffic.txt")
 CSRC = os.path.join(ROOT, "precision_flashattention_numerics_amd", "csrc")
 
 # Kernel symbols (substrings) of the profiled launches.
-K_PREFILL = "fwd_kernelILi128ELb1ELb0E"      # PASA prefill, head_dim 128, causal
-K_NAIVE = "fwd_kernelILi128ELb1ELb1E"        # naive fp16 prefill, same shape
+K_PREFILL = "fwd_kernelILi128ELb1ELi0E"      # PASA prefill, head_dim 128, causal
+K_STRICT = "fwd_kernelILi128ELb1ELi1E"       # strict PASA prefill, same shape
+K_NAIVE = "fwd_kernelILi128ELb1ELi2E"        # naive fp16 prefill, same shape
 K_SPLIT = "decode_split_kernelILi128E"       # decode split, head_dim 128
 K_COMBINE = "decode_combine_kernel"
 
 PROFILE_CMDS = {
     "trace": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/trace -o run --output-format csv "
-             "-- python bench.py --steps 20 --warmup 5 --no-cpu-baseline",
+             "-- python bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-other-configs",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/fetch -o run --output-format csv "
-             "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+             "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-other-configs",
     "write": "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/write -o run --output-format csv "
-             "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+             "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-other-configs",
     "cfetch": "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/cfetch -o run --output-format csv "
               "-- python bench.py --calibrate-copy 1024",
     "cwrite": "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/cwrite -o run --output-format csv "
               "-- python bench.py --calibrate-copy 1024",
     "pmc1": "rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU "
             "SQ_INSTS_VMEM SQ_BUSY_CYCLES SQ_WAVE_CYCLES -d gpurun_out/prof/pmc1 -o run "
-            "--output-format csv -- python bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+            "--output-format csv -- python bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-other-configs",
     "pmc2": "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU "
             "SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_ACTIVE_INST_ANY SQ_WAIT_ANY GRBM_GUI_ACTIVE "
             "-d gpurun_out/prof/pmc2 -o run --output-format csv -- python bench.py --steps 3 "
-            "--warmup 1 --no-cpu-baseline",
+            "--warmup 1 --no-cpu-baseline --no-other-configs",
 }
 
 
@@ -144,11 +145,13 @@ def summarize_profile(d):
                  f"({wd.io_bytes()/avg_s/1e3/PEAK_HBM_GBPS:.3f} of 8000)")
     lines.append(f"pasa decode combine (c5)     {int(cb['Calls']):6d} {avg_c:8.2f} "
                  f"{float(cb['MinNs'])*1e-3:8.2f} {float(cb['MaxNs'])*1e-3:8.2f}")
-    try:
-        nv = st(K_NAIVE)
-        lines.append(f"naive fp16 prefill (c2)      {int(nv['Calls']):6d} {float(nv['AverageNs'])*1e-3:8.2f}")
-    except KeyError:
-        pass
+    for label, key in (("naive fp16 prefill (c2)", K_NAIVE), ("strict PASA prefill (c2)", K_STRICT)):
+        try:
+            kv = st(key)
+        except KeyError:
+            continue
+        lines.append(f"{label:<28} {int(kv['Calls']):6d} {float(kv['AverageNs'])*1e-3:8.2f} "
+                     f"{float(kv['MinNs'])*1e-3:8.2f} {float(kv['MaxNs'])*1e-3:8.2f}")
     open(os.path.join(PROFILES, "prefill_c2_decode_c5_kernel_trace.txt"), "w").write("\n".join(lines) + "\n")
 
     fetch = _counters(os.path.join(d, "fetch", "run_counter_collection.csv"))
@@ -204,6 +207,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing and the sampled parity check")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the latency / throughput lines of the other prefill configs "
+                         "(c1, c3, c4); profiling runs use this so that the c2 kernel's "
+                         "averages are its own")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
@@ -279,22 +286,25 @@ def main():
         decode()
     torch.cuda.synchronize()
 
+    # K steps: the K prefill launches back to back, then the K decode launches,
+    # each run bracketed by events on the launch stream, so that a kernel's
+    # average is its launch-to-launch time (as rocprofv3 reports it) rather
+    # than including an event round trip per launch
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev[0].record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
         prefill()
-        ev[i][1].record(stream)
+    ev[1].record(stream)
+    for i in range(K):
         decode()
-        ev[i][2].record(stream)
+    ev[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
-    dec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
-    pre_avg = sum(pre_ms) / K
-    dec_avg = sum(dec_ms) / K
+    pre_avg = ev[0].elapsed_time(ev[1]) / K
+    dec_avg = ev[1].elapsed_time(ev[2]) / K
     log(f"timed {K} steps: prefill {pre_avg:.4f} ms, decode {dec_avg:.4f} ms, wall {wall:.3f} s")
 
     traffic_p, traffic_d = recorded_traffic()
@@ -324,6 +334,36 @@ def main():
     out["strict_tflops"] = round(flops / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e12, 3)
     os_np, ls_np = os_.cpu().numpy(), ls_.cpu().numpy()
     out["strict_nonfinite"] = nonfinite(os_np)
+
+    # the other prefill configs, outside the timed steps: c1 is launch-bound
+    # (its latency is reported), c3 and c4 against the same MFMA peak
+    if not args.no_other_configs:
+        other = {}
+        for name, reps in (("c1", 20), ("c3", 10), ("c4", 3)):
+            w = W.CONFIGS[name]
+            log(f"config {name} ...")
+            tq, tk, tv = (torch.from_numpy(x).cuda() for x in W.generate(w))
+            o2 = torch.empty_like(tq)
+            l2 = torch.empty((w.batch, w.heads_q, w.seqlen_q), dtype=torch.float32, device="cuda")
+            for _ in range(2):
+                pasa.attn_fwd(tq, tk, tv, causal=w.causal, scale=w.scale, out=o2, lse=l2)
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                pasa.attn_fwd(tq, tk, tv, causal=w.causal, scale=w.scale, out=o2, lse=l2)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ts.sort()
+            med = ts[len(ts) // 2]
+            tf = w.flops() / (med * 1e-3) / 1e12
+            other[name] = {"median_ms": round(med, 5), "min_ms": round(ts[0], 5),
+                           "tflops": round(tf, 2), "frac": round(tf / 2500.0, 4),
+                           "nonfinite": nonfinite(o2.cpu().numpy())}
+            del tq, tk, tv, o2, l2
+            torch.cuda.empty_cache()
+        out["other_configs"] = other
 
     cpu = None
     if not args.no_cpu_baseline:

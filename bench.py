@@ -363,6 +363,31 @@ def main():
                            "nonfinite": nonfinite(o2.cpu().numpy())}
             del tq, tk, tv, o2, l2
             torch.cuda.empty_cache()
+        # the decode workload over a paged cache: 64-key pages scattered over
+        # the pool in a seeded random order (HBM-bound like the contiguous one)
+        ps = 64
+        n_pages = wd.batch * wd.seqlen_kv // ps
+        perm = torch.from_numpy(np.random.default_rng(5).permutation(n_pages).astype(np.int32)).cuda()
+        kpool = torch.empty((n_pages, ps, wd.heads_kv, wd.head_dim), dtype=torch.float16, device="cuda")
+        vpool = torch.empty_like(kpool)
+        kpool[perm.long()] = tkd.reshape(n_pages, ps, wd.heads_kv, wd.head_dim)
+        vpool[perm.long()] = tvd.reshape(n_pages, ps, wd.heads_kv, wd.head_dim)
+        table = perm.reshape(wd.batch, wd.seqlen_kv // ps).contiguous()
+        lens = torch.full((wd.batch,), wd.seqlen_kv, dtype=torch.int32, device="cuda")
+        opg, lpg = pasa.attn_decode_paged(tqd, kpool, vpool, table, lens, scale=wd.scale)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            pasa.attn_decode_paged(tqd, kpool, vpool, table, lens, scale=wd.scale, out=opg, lse=lpg)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pg_ms = e0.elapsed_time(e1) / 10
+        other["c5_paged64"] = {"ms": round(pg_ms, 5),
+                               "GBps": round(wd.io_bytes() / (pg_ms * 1e-3) / 1e9, 1),
+                               "frac": round(wd.io_bytes() / (pg_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                               "equal_to_contiguous": bool(torch.equal(opg, od))}
+        del kpool, vpool
+        torch.cuda.empty_cache()
         out["other_configs"] = other
 
     cpu = None

@@ -133,6 +133,38 @@ int pasa_attn_decode(const void* q, const void* k_cache, const void* v_cache, vo
                      int head_dim, float softmax_scale, int num_splits, void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Split-KV decode over a paged KV cache (one query token per sequence).  The
+ * operation is pasa_attn_decode's: the same PASA tile numerics per split and
+ * the same merge of the normalised partials ("Block Sparse Flash Attention"
+ * topic page, FoldAttention card); only the cache layout differs, and that
+ * layout is this library's choice, not the pages'.
+ *   k_pages, v_pages  device fp16 [num_pages, page_size, num_heads_q/gqa_group,
+ *                     head_dim]: a pool of pages of page_size keys each.
+ *   block_table  device int32 [batch, max_pages_per_seq]: key j of sequence b
+ *                is row j % page_size of page block_table[b][j / page_size].
+ *   seq_lens     device int32 [batch]: key count of each sequence, read on the
+ *                device (no host synchronisation); values are clamped to
+ *                [0, page_size * max_pages_per_seq].  A sequence of length 0
+ *                gets o = 0 and lse = -inf.
+ *   q, o, lse, softmax_scale, num_splits, workspace, stream: as
+ *                pasa_attn_decode, with page_size * max_pages_per_seq standing
+ *                for seqlen_kv (the splits are cut from that bound; splits past
+ *                a sequence's end contribute nothing).
+ * page_size must be a multiple of 32.  Entries of block_table that a sequence's
+ * keys use must lie in [0, num_pages); an entry outside that range reads as
+ * zero keys and values instead of faulting.
+ * Errors: as pasa_attn_decode, plus PASA_ERR_INVALID for a null block_table or
+ * seq_lens or a page_size, num_pages or max_pages_per_seq < 1, and
+ * PASA_ERR_UNSUPPORTED for a page_size that is not a multiple of 32.
+ */
+int pasa_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                           const int* block_table, const int* seq_lens, void* o, float* lse,
+                           int batch, int num_heads_q, int gqa_group, int head_dim, int page_size,
+                           int num_pages, int max_pages_per_seq, float softmax_scale,
+                           int num_splits, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 /* The split count pasa_attn_decode uses for num_splits = 0 (host function, no
  * device work): enough (sequence, key/value head, split) work items to fill the
  * chip, clamped to the number of 32-key sub-tiles.  Returns 0 on invalid sizes. */

@@ -32,6 +32,9 @@ _lib.pasa_naive_attn_fwd.restype = _i
 _lib.pasa_attn_fwd_strict.argtypes = _lib.pasa_attn_fwd.argtypes
 _lib.pasa_attn_fwd_strict.restype = _i
 _lib.pasa_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
+_lib.pasa_attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                        _i, _f, _i, _vp, _sz, _vp]
+_lib.pasa_attn_decode_paged.restype = _i
 _lib.pasa_attn_decode.restype = _i
 _lib.pasa_attn_decode_splits.argtypes = [_i, _i, _i, _i]
 _lib.pasa_attn_decode_splits.restype = _i
@@ -174,6 +177,45 @@ def attn_decode(q, k_cache, v_cache, num_splits=0, scale=None, out=None, lse=Non
                                _ptr(workspace), workspace.numel() * workspace.element_size(),
                                _stream(stream))
     _check(rc, "pasa_attn_decode")
+    return (out, lse) if return_lse or lse is not None else out
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, num_splits=0, scale=None,
+                      out=None, lse=None, workspace=None, return_lse=True, stream=None):
+    """Split-KV PASA decode over a paged cache.  q [B,1,Hq,D]; pages
+    [num_pages, page_size, Hkv, D]; block_table int32 [B, max_pages];
+    seq_lens int32 [B] -> (o, lse [B,Hq])."""
+    for t, nm in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+        _want(t, nm)
+    _want(block_table, "block_table", torch.int32)
+    _want(seq_lens, "seq_lens", torch.int32)
+    if q.dim() != 4 or q.shape[1] != 1 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError("q must be [B,1,Hq,D]; pages [num_pages,page_size,Hkv,D]")
+    B, _, Hq, D = q.shape
+    num_pages, page_size, Hkv, Dk = k_pages.shape
+    if Dk != D or Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError("inconsistent q/page shapes")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages], seq_lens [B]")
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = D ** -0.5
+    if workspace is None:
+        n = num_splits or decode_splits(B, page_size * max_pages, Hq, Hq // Hkv)
+        nbytes = decode_workspace_bytes(B, Hq, D, n)
+        ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=q.device)
+        off = (-ws.data_ptr()) % 256
+        workspace = ws[off:off + nbytes]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    rc = _lib.pasa_attn_decode_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(out),
+        _ptr(lse), B, Hq, Hq // Hkv, D, page_size, num_pages, max_pages, float(scale),
+        int(num_splits), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(rc, "pasa_attn_decode_paged")
     return (out, lse) if return_lse or lse is not None else out
 
 

@@ -33,6 +33,11 @@ struct DecodeArgs {
 enum { kVarPasa = 0, kVarStrict = 1, kVarNaive = 2 };
 hipError_t launch_fwd(const FwdArgs& a, int variant, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream);
+// Same over a paged cache (a.k / a.v are the page pools, a.seqlen_kv the
+// longest key count the block table can address).
+hipError_t launch_decode_split_paged(const DecodeArgs& a, const int* block_table,
+                                     const int* seq_lens, int page_size, int max_pages,
+                                     int num_pages, hipStream_t stream);
 hipError_t launch_decode_combine(const float* o_part, const float* lse_part, void* o, float* lse,
                                  int batch, int num_heads_q, int head_dim, int num_splits,
                                  hipStream_t stream);

@@ -33,6 +33,10 @@ int check_common(const void* q, const void* k, const void* v, const void* o, int
     if (!fits(batch, seqlen_q, num_heads_q, head_dim) ||
         !fits(batch, seqlen_kv, num_heads_q, head_dim))
         return PASA_ERR_UNSUPPORTED;
+    // one head's K/V slab of one sequence is addressed through a buffer
+    // descriptor: 32-bit byte offsets
+    if ((int64_t)seqlen_kv * (num_heads_q / gqa_group) * head_dim * 2 > 0xFFFFFFFFLL)
+        return PASA_ERR_UNSUPPORTED;
     if (seqlen_q > 65535 * 128) return PASA_ERR_UNSUPPORTED;   // grid y limit
     if (batch > 65535) return PASA_ERR_UNSUPPORTED;            // grid z limit
     return PASA_OK;
@@ -123,6 +127,49 @@ int pasa_attn_decode(const void* q, const void* k_cache, const void* v_cache, vo
     pasa::DecodeArgs a{q, k_cache, v_cache, o_part, lse_part, batch, seqlen_kv, num_heads_q,
                        gqa_group, head_dim, softmax_scale, n};
     if (pasa::launch_decode_split(a, stream) != hipSuccess) return PASA_ERR_HIP;
+    if (pasa::launch_decode_combine(o_part, lse_part, o, lse, batch, num_heads_q, head_dim, n,
+                                    stream) != hipSuccess)
+        return PASA_ERR_HIP;
+    return PASA_OK;
+}
+
+int pasa_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                           const int* block_table, const int* seq_lens, void* o, float* lse,
+                           int batch, int num_heads_q, int gqa_group, int head_dim, int page_size,
+                           int num_pages, int max_pages_per_seq, float softmax_scale,
+                           int num_splits, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+    if (!block_table || !seq_lens) return PASA_ERR_INVALID;
+    if (page_size < 1 || num_pages < 1 || max_pages_per_seq < 1) return PASA_ERR_INVALID;
+    if (page_size % pasa::kDecodeBlock != 0) return PASA_ERR_UNSUPPORTED;
+    const int64_t max_keys = (int64_t)page_size * max_pages_per_seq;
+    if (max_keys > 0x7fffffff) return PASA_ERR_UNSUPPORTED;
+    const int seqlen_kv = (int)max_keys;
+    // the shape checks of the contiguous decode, with the pool as one "sequence"
+    int rc = check_common(q, k_pages, v_pages, o, batch, 1, seqlen_kv, num_heads_q, gqa_group,
+                          head_dim, softmax_scale);
+    if (rc != PASA_OK) return rc;
+    if (!fits(num_pages, page_size, num_heads_q / gqa_group, head_dim)) return PASA_ERR_UNSUPPORTED;
+    if ((int64_t)batch * max_pages_per_seq > 0x7fffffff) return PASA_ERR_UNSUPPORTED;
+    if (num_splits < 0) return PASA_ERR_INVALID;
+    int n = num_splits == 0 ? pasa_attn_decode_splits(batch, seqlen_kv, num_heads_q, gqa_group)
+                            : num_splits;
+    const int blocks = (seqlen_kv + pasa::kDecodeBlock - 1) / pasa::kDecodeBlock;
+    if (n > blocks) n = blocks;
+    if (n > 65535) return PASA_ERR_UNSUPPORTED;
+    const int per_split = (blocks + n - 1) / n * pasa::kDecodeBlock;
+    if (per_split > kMaxFp16Sum) return PASA_ERR_UNSUPPORTED;
+    const size_t need = pasa_attn_decode_workspace_bytes(batch, num_heads_q, head_dim, n);
+    if (workspace == nullptr || ((uintptr_t)workspace & 255) != 0 || workspace_bytes < need)
+        return PASA_ERR_WORKSPACE;
+    const size_t rows = (size_t)batch * num_heads_q * n;
+    float* o_part = (float*)workspace;
+    float* lse_part = (float*)((char*)workspace + align256(rows * head_dim * sizeof(float)));
+    pasa::DecodeArgs a{q, k_pages, v_pages, o_part, lse_part, batch, seqlen_kv, num_heads_q,
+                       gqa_group, head_dim, softmax_scale, n};
+    if (pasa::launch_decode_split_paged(a, block_table, seq_lens, page_size, max_pages_per_seq,
+                                        num_pages, stream) != hipSuccess)
+        return PASA_ERR_HIP;
     if (pasa::launch_decode_combine(o_part, lse_part, o, lse, batch, num_heads_q, head_dim, n,
                                     stream) != hipSuccess)
         return PASA_ERR_HIP;

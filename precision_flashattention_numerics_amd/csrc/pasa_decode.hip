@@ -19,6 +19,13 @@
 // computes on the current one; it synchronises only with itself
 // (s_waitcnt vmcnt), never with other waves.  Every wave writes one fp32
 // partial (o_s, lse_s).
+// Paged variant (PAGED = true): the cache is a pool of pages of page_size
+// keys ([num_pages, page_size, Hkv, D]); sequence b's key j lives in page
+// block_table[b][j / page_size] at row j % page_size, and its length is
+// seq_lens[b], read on the device.  page_size is a multiple of 32, so a
+// sub-tile never straddles pages; each sub-tile gets its own buffer
+// descriptor bounded by the sequence end, and an out-of-range page index
+// reads as zeros instead of faulting.
 // Combine kernel: one workgroup per (sequence, query head), one thread per
 // head-dim column.
 
@@ -39,11 +46,17 @@ constexpr int dec_smem_bytes() { return kSlots * 2 * sub_halves<D>() * 2; }
 template <int D>
 constexpr int dma_per_sub() { return 2 * (kSub * D / 8) / 64; }     // 16-byte-per-lane loads
 
-template <int D>
+struct Paging {
+    const int* block_table;   // [batch, max_pages] page indices
+    const int* seq_lens;      // [batch] key counts
+    int page_size, max_pages, num_pages;
+};
+
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64) void decode_split_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, float* __restrict__ o_part, float* __restrict__ lse_part,
-    int Skv, int Hq, int group, float c, int split_len, int head_chunks, int nsplit) {
+    int Skv, int Hq, int group, float c, int split_len, int head_chunks, int nsplit, Paging pg) {
     constexpr int KK = D / 16;
     constexpr int DT = D / 32;
     constexpr int NL = dma_per_sub<D>();
@@ -67,12 +80,17 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     const int hq = hkv * group + hloc;
 
     const int64_t kv_stride = (int64_t)Hkv * D;
+    const uint32_t stride_b = (uint32_t)(kv_stride * 2);
+    if (PAGED) {   // this sequence's length, clamped to what its block table can address
+        const int len = __builtin_amdgcn_readfirstlane(pg.seq_lens[b]);
+        Skv = max(0, min(len, pg.max_pages * pg.page_size));
+    }
     const _Float16* kb = k + ((int64_t)b * Skv * Hkv + hkv) * D;
     const _Float16* vb = v + ((int64_t)b * Skv * Hkv + hkv) * D;
-    const uint32_t slab_bytes = (uint32_t)(((int64_t)(Skv - 1) * kv_stride + D) * 2);
+    const uint32_t slab_bytes =
+        PAGED ? 0u : (uint32_t)(((int64_t)(Skv - 1) * kv_stride + D) * 2);
     const i32x4 krs = make_rsrc(kb, slab_bytes);
     const i32x4 vrs = make_rsrc(vb, slab_bytes);
-    const uint32_t stride_b = (uint32_t)(kv_stride * 2);
 
     const int kbeg = min(split * split_len, Skv);
     const int kend = min(kbeg + split_len, Skv);
@@ -81,8 +99,23 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     auto slot_k = [&](int j) { return smem + (j % kSlots) * 2 * sub_halves<D>(); };
     auto issue = [&](int j) {
         _Float16* sk = slot_k(j);
-        stage_tile<D, kSub, 1, false>(krs, stride_b, kbeg + j * kSub, sk, 0, lane);
-        stage_tile<D, kSub, 1, true>(vrs, stride_b, kbeg + j * kSub, sk + sub_halves<D>(), 0, lane);
+        const int key0 = kbeg + j * kSub;
+        if (PAGED) {
+            // the sub-tile's page, and a descriptor over its rows that exist
+            const int page = __builtin_amdgcn_readfirstlane(
+                pg.block_table[(int64_t)b * pg.max_pages + key0 / pg.page_size]);
+            const int rows = min(kSub, Skv - key0);
+            const bool ok = page >= 0 && page < pg.num_pages;
+            const int64_t base = ((int64_t)(ok ? page : 0) * pg.page_size + key0 % pg.page_size) *
+                                     kv_stride + (int64_t)hkv * D;
+            const uint32_t bytes = ok ? (uint32_t)(((int64_t)(rows - 1) * kv_stride + D) * 2) : 0u;
+            stage_tile<D, kSub, 1, false>(make_rsrc(k + base, bytes), stride_b, 0, sk, 0, lane);
+            stage_tile<D, kSub, 1, true>(make_rsrc(v + base, bytes), stride_b, 0,
+                                         sk + sub_halves<D>(), 0, lane);
+        } else {
+            stage_tile<D, kSub, 1, false>(krs, stride_b, key0, sk, 0, lane);
+            stage_tile<D, kSub, 1, true>(vrs, stride_b, key0, sk + sub_halves<D>(), 0, lane);
+        }
     };
 
     h8 qreg[KK];
@@ -176,11 +209,12 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(
     if (lse != nullptr && d == 0) lse[row] = L;
 }
 
-template <int D>
-hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
-    auto kern = decode_split_kernel<D>;
+template <int D, bool PAGED>
+hipError_t launch_split(const DecodeArgs& a, const Paging& pg, hipStream_t stream) {
+    auto kern = decode_split_kernel<D, PAGED>;
     constexpr int smem = dec_smem_bytes<D>();
     static_assert(smem <= 64 * 1024, "dynamic LDS above 64 KB would need an opt-in");
+    // seqlen_kv is the (upper bound of the) key count the splits are cut from
     const int subs = (a.seqlen_kv + kSub - 1) / kSub;
     const int per_split = (subs + a.num_splits - 1) / a.num_splits;
     const int head_chunks = (a.gqa_group + 31) / 32;
@@ -188,14 +222,24 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(kern, dim3((unsigned)waves), dim3(64), smem, stream,
                        (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
                        a.o_part, a.lse_part, a.seqlen_kv, a.num_heads_q, a.gqa_group,
-                       a.softmax_scale * kLog2e, per_split * kSub, head_chunks, a.num_splits);
+                       a.softmax_scale * kLog2e, per_split * kSub, head_chunks, a.num_splits, pg);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream) {
-    return a.head_dim == 128 ? launch_split<128>(a, stream) : launch_split<64>(a, stream);
+    const Paging none{nullptr, nullptr, 0, 0, 0};
+    return a.head_dim == 128 ? launch_split<128, false>(a, none, stream)
+                             : launch_split<64, false>(a, none, stream);
+}
+
+hipError_t launch_decode_split_paged(const DecodeArgs& a, const int* block_table,
+                                     const int* seq_lens, int page_size, int max_pages,
+                                     int num_pages, hipStream_t stream) {
+    const Paging pg{block_table, seq_lens, page_size, max_pages, num_pages};
+    return a.head_dim == 128 ? launch_split<128, true>(a, pg, stream)
+                             : launch_split<64, true>(a, pg, stream);
 }
 
 hipError_t launch_decode_combine(const float* o_part, const float* lse_part, void* o, float* lse,

@@ -29,6 +29,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared()
     for fn in ("pasa_attn_fwd", "pasa_attn_fwd_strict", "pasa_naive_attn_fwd", "pasa_attn_decode",
+               "pasa_attn_decode_paged",
                "pasa_attn_decode_combine", "pasa_attn_decode_workspace_bytes",
                "pasa_attn_decode_splits", "pasa_status_string"):
         assert fn in names

@@ -101,6 +101,23 @@ def test_strict_small_shapes_vs_oracle(pasa, shape):
     assert lse_ok(lse, rl)
 
 
+@pytest.mark.parametrize("Sq,Skv", [(1024, 5120), (640, 8192), (1, 3000)])
+def test_chunked_prefill_against_cache_vs_oracle(pasa, Sq, Skv):
+    """A chunk of new queries against a cache that already holds earlier keys:
+    bottom-right causal alignment (query i sees keys j <= i + Skv - Sq)."""
+    w = W.custom(1, Sq, Skv, 28, 4, 128, True, kind="bias", seed=Sq + Skv, bias=30.0)
+    say("chunked prefill", Sq, Skv)
+    (q, k, v), o, lse = run_fwd(pasa, w)
+    rows = sample_rows(w, 400, np.random.default_rng(Sq))
+    ro, rl = attn_fp64(q, k, v, w.scale, True, rows=rows)
+    go, gl = gather_rows(o, lse, w, rows)
+    assert nonfinite(o) == 0
+    err = rel_rmse(go, ro)
+    say("rel_rmse", err)
+    assert err <= REL_RMSE_MAX
+    assert lse_ok(gl, rl)
+
+
 def test_c4_sampled_rows_vs_oracle(pasa):
     w = W.CONFIGS["c4"]
     say("config c4 (sampled rows)")

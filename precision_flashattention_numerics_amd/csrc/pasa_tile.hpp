@@ -204,83 +204,6 @@ __device__ __forceinline__ float row_sum(const RowState& st) {
     return NAIVE ? st.lsum : (float)st.lhi + (float)st.llo;
 }
 
-// Cooperative staging of one block of BKEYS keys x D head-dim columns:
-// K kept row-major (row stride KPAD halves), V transposed (V^T, row stride
-// VPAD halves) so that the P V product reads 8 consecutive keys per lane.
-template <int D, int BKEYS, int THREADS>
-struct Stager {
-    static constexpr int KPAD = D + 8;        // 16-byte pad: conflict-free 16 B reads
-    static constexpr int VPAD = BKEYS + 8;
-    static constexpr int K_HALVES = BKEYS * KPAD;
-    static constexpr int V_HALVES = D * VPAD;
-    static constexpr int STAGE_HALVES = K_HALVES + V_HALVES;
-    static constexpr int KCH = (BKEYS * D / 8 + THREADS - 1) / THREADS;  // 16 B K chunks per thread
-    static constexpr int VUNITS = (BKEYS / 4) * (D / 8);                 // 4 keys x 8 columns
-    static constexpr int VCH = (VUNITS + THREADS - 1) / THREADS;
-
-    h8 kreg[KCH];
-    h8 vreg[VCH][4];
-
-    __device__ __forceinline__ void load(const _Float16* kb, const _Float16* vb,
-                                         int64_t stride, int base, int nkeys, int tid) {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int chunk = tid + THREADS * i;
-            const int row = chunk / (D / 8), col = chunk % (D / 8);
-            const int key = base + row;
-            kreg[i] = (chunk < BKEYS * D / 8 && key < nkeys)
-                          ? *(const h8*)(kb + (int64_t)key * stride + 8 * col)
-                          : (h8){};
-        }
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-            const int u = tid + THREADS * i;
-            const int kg = u % (BKEYS / 4), dg = u / (BKEYS / 4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = base + 4 * kg + r;
-                vreg[i][r] = (u < VUNITS && key < nkeys)
-                                 ? *(const h8*)(vb + (int64_t)key * stride + 8 * dg)
-                                 : (h8){};
-            }
-        }
-    }
-
-    __device__ __forceinline__ void store(_Float16* Ks, int tid) const {
-        _Float16* Vt = Ks + K_HALVES;
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int chunk = tid + THREADS * i;
-            if (chunk < BKEYS * D / 8) {
-                const int row = chunk / (D / 8), col = chunk % (D / 8);
-                *(h8*)(Ks + row * KPAD + 8 * col) = kreg[i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-            const int u = tid + THREADS * i;
-            if (u < VUNITS) {
-                const int kg = u % (BKEYS / 4), dg = u / (BKEYS / 4);
-                // 4 keys x 8 columns -> 8 columns x 4 keys, with byte permutes:
-                // word j of a row holds columns 2j (low half) and 2j+1 (high).
-                u4 r0 = __builtin_bit_cast(u4, vreg[i][0]);
-                u4 r1 = __builtin_bit_cast(u4, vreg[i][1]);
-                u4 r2 = __builtin_bit_cast(u4, vreg[i][2]);
-                u4 r3 = __builtin_bit_cast(u4, vreg[i][3]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const u2 lo = {__builtin_amdgcn_perm(r1[j], r0[j], 0x05040100u),
-                                   __builtin_amdgcn_perm(r3[j], r2[j], 0x05040100u)};
-                    const u2 hi = {__builtin_amdgcn_perm(r1[j], r0[j], 0x07060302u),
-                                   __builtin_amdgcn_perm(r3[j], r2[j], 0x07060302u)};
-                    *(u2*)(Vt + (8 * dg + 2 * j) * VPAD + 4 * kg) = lo;
-                    *(u2*)(Vt + (8 * dg + 2 * j + 1) * VPAD + 4 * kg) = hi;
-                }
-            }
-        }
-    }
-};
-
 // ---------------------------------------------------------------------------
 // Direct HBM -> LDS staging (buffer_load ... lds) with XOR-swizzled 16-byte
 // chunks, and the matching operand reads.
@@ -400,36 +323,6 @@ __device__ __forceinline__ void pv_chunks_tr(const _Float16* Vs, int ch0, const 
             const s4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)pb);
             const h4 ha = __builtin_bit_cast(h4, va), hb = __builtin_bit_cast(h4, vb);
             const h8 a = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
-            acc[dt] = mfma_32x32x16(a, bp, acc[dt]);
-        }
-    }
-}
-
-// S^T (32 keys x 32 query columns) for the keys at rows [row0, row0+32) of
-// the staged K tile; qreg is the B operand (query column l%32, 8 columns of
-// the head dimension per 16-wide contraction step).
-template <int D, int KPAD>
-__device__ __forceinline__ f16v qk_subtile(const _Float16* Ks, int row0, const h8 (&qreg)[D / 16],
-                                           int n, int hh) {
-    f16v s = (f16v){};
-    const _Float16* krow = Ks + (row0 + sigma(n)) * KPAD + 8 * hh;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) s = mfma_32x32x16(*(const h8*)(krow + 16 * kk), qreg[kk], s);
-    return s;
-}
-
-// O^T += V^T P^T for the 16-key chunks [16*ch0, 16*ch0 + 16*NCH) of the
-// staged V^T tile, with P from softmax_block (packed pairs).
-template <int D, int VPAD, int NCH>
-__device__ __forceinline__ void pv_chunks(const _Float16* Vt, int ch0, const h2* P,
-                                          f16v (&acc)[D / 32], int n, int hh) {
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-        const h2 p0 = P[4 * ch + 0], p1 = P[4 * ch + 1], p2 = P[4 * ch + 2], p3 = P[4 * ch + 3];
-        const h8 bp = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            const h8 a = *(const h8*)(Vt + (32 * dt + n) * VPAD + 16 * (ch0 + ch) + 8 * hh);
             acc[dt] = mfma_32x32x16(a, bp, acc[dt]);
         }
     }

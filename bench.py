@@ -388,6 +388,23 @@ def main():
                                "equal_to_contiguous": bool(torch.equal(opg, od))}
         del kpool, vpool
         torch.cuda.empty_cache()
+        # c2 with e4m3 queries and keys (per-tensor scales; values fp16)
+        q8s = float(tqp.abs().max()) / 448.0
+        k8s = float(tkp.abs().max()) / 448.0
+        q8 = torch.clamp(tqp.float() / q8s, -448.0, 448.0).to(torch.float8_e4m3fn)
+        k8 = torch.clamp(tkp.float() / k8s, -448.0, 448.0).to(torch.float8_e4m3fn)
+        o8, l8 = pasa.attn_fwd_fp8(q8, k8, tvp, q8s, k8s, causal=wp.causal, scale=wp.scale)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            pasa.attn_fwd_fp8(q8, k8, tvp, q8s, k8s, causal=wp.causal, scale=wp.scale, out=o8, lse=l8)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        f8_ms = e0.elapsed_time(e1) / 10
+        other["c2_fp8_qk"] = {"ms": round(f8_ms, 5),
+                              "tflops": round(flops / (f8_ms * 1e-3) / 1e12, 2),
+                              "nonfinite": nonfinite(o8.cpu().numpy())}
+        del q8, k8, o8, l8
         out["other_configs"] = other
 
     cpu = None

@@ -88,6 +88,30 @@ int pasa_attn_fwd_strict(const void* q, const void* k, const void* v, void* o, f
                          int head_dim, float softmax_scale, int causal, hipStream_t stream);
 
 /*
+ * PASA forward with 8-bit queries and keys: q and k hold OCP fp8 e4m3 values
+ * (1 byte each, largest finite 448, no infinities) with one dequantisation
+ * scale per tensor, v stays fp16.  The score is
+ *     S_ij = q_scale * k_scale * sum_d q8_id * k8_jd
+ * formed on the fp8 matrix cores with fp32 accumulation; everything after the
+ * score -- the pseudo-average shift, the fp16 tile, exponentials, statistics,
+ * P V and the epilogue -- is pasa_attn_fwd's.  The method's fp16 range
+ * argument ("Online Pseudo-average Shifting Attention (PASA) ...", Abstract:
+ * overflow above 65504) is unchanged: the dot products of e4m3 inputs can
+ * still exceed it.  Producing the e4m3 inputs (rounding, saturation, scale
+ * choice) is the caller's.
+ *   q  device e4m3 [batch, seqlen_q, num_heads_q, head_dim]
+ *   k  device e4m3 [batch, seqlen_kv, num_heads_q / gqa_group, head_dim]
+ *   v, o, lse, softmax_scale, causal, stream: as pasa_attn_fwd.
+ *   q_scale, k_scale  positive finite dequantisation factors.
+ * Errors: as pasa_attn_fwd, plus PASA_ERR_UNSUPPORTED for a non-positive or
+ * non-finite q_scale, k_scale or product with softmax_scale.
+ */
+int pasa_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group,
+                      int head_dim, float softmax_scale, float q_scale, float k_scale, int causal,
+                      hipStream_t stream);
+
+/*
  * Naive fp16 Flash-Attention forward: the same blockwise kernel WITHOUT the
  * pseudo-average shift.  The unscaled score tile QK^T is rounded to fp16 and
  * then multiplied by the scale in fp16, as a plain half-precision Flash

@@ -31,6 +31,9 @@ _lib.pasa_naive_attn_fwd.argtypes = _lib.pasa_attn_fwd.argtypes
 _lib.pasa_naive_attn_fwd.restype = _i
 _lib.pasa_attn_fwd_strict.argtypes = _lib.pasa_attn_fwd.argtypes
 _lib.pasa_attn_fwd_strict.restype = _i
+_lib.pasa_attn_fwd_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _f, _f, _i,
+                                   _vp]
+_lib.pasa_attn_fwd_fp8.restype = _i
 _lib.pasa_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
 _lib.pasa_attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                                         _i, _f, _i, _vp, _sz, _vp]
@@ -125,6 +128,32 @@ def attn_fwd_strict(q, k, v, causal=False, scale=None, out=None, lse=None, retur
     """PASA forward with fp16 running maximum and offset as well; same interface."""
     return _fwd(_lib.pasa_attn_fwd_strict, "pasa_attn_fwd_strict", q, k, v, causal, scale, out,
                 lse, return_lse, stream)
+
+
+def attn_fwd_fp8(q8, k8, v, q_scale, k_scale, causal=False, scale=None, out=None, lse=None,
+                 return_lse=True, stream=None):
+    """PASA forward with e4m3 queries and keys (torch.float8_e4m3fn, one
+    dequantisation scale each) and fp16 values -> (o fp16, lse)."""
+    _want(q8, "q8", torch.float8_e4m3fn)
+    _want(k8, "k8", torch.float8_e4m3fn)
+    _want(v, "v")
+    if q8.dim() != 4 or k8.dim() != 4 or v.shape != k8.shape:
+        raise ValueError("q8 [B,Sq,Hq,D], k8 and v [B,Skv,Hkv,D]")
+    B, Sq, Hq, D = q8.shape
+    Bk, Skv, Hkv, Dk = k8.shape
+    if Bk != B or Dk != D or Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError("inconsistent q/k/v shapes")
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty(q8.shape, dtype=torch.float16, device=q8.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
+    rc = _lib.pasa_attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Skv, Hq,
+                                Hq // Hkv, D, float(scale), float(q_scale), float(k_scale),
+                                int(bool(causal)), _stream(stream))
+    _check(rc, "pasa_attn_fwd_fp8")
+    return (out, lse) if return_lse or lse is not None else out
 
 
 def naive_attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, return_lse=True,

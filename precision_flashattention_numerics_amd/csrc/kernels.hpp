@@ -15,6 +15,7 @@ struct FwdArgs {
     int batch, seqlen_q, seqlen_kv, num_heads_q, gqa_group, head_dim;
     float softmax_scale;
     int causal;
+    float qk_dequant = 1.0f;   // fp8 variant: q_scale * k_scale
 };
 
 struct DecodeArgs {
@@ -28,9 +29,9 @@ struct DecodeArgs {
     int num_splits;
 };
 
-// Forward variants: PASA, PASA with fp16 running maximum and offset, and the
-// naive fp16 Flash-Attention overflow exhibit.
-enum { kVarPasa = 0, kVarStrict = 1, kVarNaive = 2 };
+// Forward variants: PASA, PASA with fp16 running maximum and offset, the
+// naive fp16 Flash-Attention overflow exhibit, and PASA with e4m3 Q and K.
+enum { kVarPasa = 0, kVarStrict = 1, kVarNaive = 2, kVarFp8 = 3 };
 hipError_t launch_fwd(const FwdArgs& a, int variant, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream);
 // Same over a paged cache (a.k / a.v are the page pools, a.seqlen_kv the

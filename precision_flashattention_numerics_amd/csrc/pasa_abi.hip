@@ -44,14 +44,15 @@ int check_common(const void* q, const void* k, const void* v, const void* o, int
 
 int fwd_common(int variant, const void* q, const void* k, const void* v, void* o, float* lse,
                int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group,
-               int head_dim, float softmax_scale, int causal, hipStream_t stream) {
+               int head_dim, float softmax_scale, int causal, hipStream_t stream,
+               float qk_dequant = 1.0f) {
     int rc = check_common(q, k, v, o, batch, seqlen_q, seqlen_kv, num_heads_q, gqa_group,
                           head_dim, softmax_scale);
     if (rc != PASA_OK) return rc;
     if (causal != 0 && causal != 1) return PASA_ERR_INVALID;
     if (seqlen_kv > kMaxFp16Sum) return PASA_ERR_UNSUPPORTED;
     pasa::FwdArgs a{q, k, v, o, lse, batch, seqlen_q, seqlen_kv, num_heads_q, gqa_group,
-                    head_dim, softmax_scale, causal};
+                    head_dim, softmax_scale, causal, qk_dequant};
     return pasa::launch_fwd(a, variant, stream) == hipSuccess ? PASA_OK : PASA_ERR_HIP;
 }
 
@@ -73,6 +74,18 @@ int pasa_attn_fwd_strict(const void* q, const void* k, const void* v, void* o, f
                          int head_dim, float softmax_scale, int causal, hipStream_t stream) {
     return fwd_common(pasa::kVarStrict, q, k, v, o, lse, batch, seqlen_q, seqlen_kv, num_heads_q,
                       gqa_group, head_dim, softmax_scale, causal, stream);
+}
+
+int pasa_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group,
+                      int head_dim, float softmax_scale, float q_scale, float k_scale, int causal,
+                      hipStream_t stream) {
+    if (!(q_scale > 0.0f) || !isfinite(q_scale) || !(k_scale > 0.0f) || !isfinite(k_scale))
+        return PASA_ERR_UNSUPPORTED;
+    const float dq = q_scale * k_scale;
+    if (!(dq > 0.0f) || !isfinite(dq) || !isfinite(softmax_scale * dq)) return PASA_ERR_UNSUPPORTED;
+    return fwd_common(pasa::kVarFp8, q, k, v, o, lse, batch, seqlen_q, seqlen_kv, num_heads_q,
+                      gqa_group, head_dim, softmax_scale, causal, stream, dq);
 }
 
 int pasa_naive_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -95,6 +95,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     int B, int Sq, int Skv, int Hq, int group, float c, int n_qtiles) {
     constexpr bool NAIVE = VAR == kVarNaive;
     constexpr bool STRICT = VAR == kVarStrict;
+    constexpr bool FP8 = VAR == kVarFp8;       // q and k are e4m3 bytes
+    constexpr int EB = FP8 ? 1 : 2;            // bytes per q / k element
     constexpr int KK = D / 16;
     constexpr int DT = D / 32;
     extern __shared__ __attribute__((aligned(1024))) _Float16 smem[];
@@ -116,11 +118,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     const int64_t q_stride = (int64_t)Hq * D;
     const int64_t kv_stride = (int64_t)Hkv * D;
-    const _Float16* qb = q + ((int64_t)b * Sq * Hq + hq) * D;
-    const _Float16* kb = k + ((int64_t)b * Skv * Hkv + hkv) * D;
+    const uint8_t* qb = (const uint8_t*)q + ((int64_t)b * Sq * Hq + hq) * D * EB;
+    const uint8_t* kb = (const uint8_t*)k + ((int64_t)b * Skv * Hkv + hkv) * D * EB;
     const _Float16* vb = v + ((int64_t)b * Skv * Hkv + hkv) * D;
     const uint32_t slab_bytes = (uint32_t)(((int64_t)(Skv - 1) * kv_stride + D) * 2);
-    const i32x4 krs = make_rsrc(kb, slab_bytes);
+    const i32x4 krs = make_rsrc(kb, (uint32_t)(((int64_t)(Skv - 1) * kv_stride + D) * EB));
     const i32x4 vrs = make_rsrc(vb, slab_bytes);
     const uint32_t stride_b = (uint32_t)(kv_stride * 2);
 
@@ -145,8 +147,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     _Float16* const Kst = smem;                           // 2 stages of K
     _Float16* const Vst = smem + 2 * tile_halves<D>();    // 2 stages of V
     auto load_k = [&](int blk) {
-        stage_tile<D, kBC, kWaves, false>(krs, stride_b, blk * kBC,
-                                          Kst + (blk & 1) * tile_halves<D>(), w, lane);
+        if constexpr (FP8)
+            stage_tile_f8<D, kBC, kWaves>(krs, (uint32_t)kv_stride, blk * kBC,
+                                          (uint8_t*)(Kst + (blk & 1) * tile_halves<D>()), w, lane);
+        else
+            stage_tile<D, kBC, kWaves, false>(krs, stride_b, blk * kBC,
+                                              Kst + (blk & 1) * tile_halves<D>(), w, lane);
     };
     auto load_v = [&](int blk) {
         stage_tile<D, kBC, kWaves, true>(vrs, stride_b, blk * kBC,
@@ -155,10 +161,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (nblocks > 0) load_k(0);
 
     // ---- Q operand: lane holds Q[qi][16*kk + 8*hh .. +7]
-    h8 qreg[KK];
+    h8 qreg[FP8 ? 1 : KK];
+    v8i q8reg[FP8 ? D / 64 : 1];
+    if constexpr (FP8) {
+        // lane holds Q[qi][64*kk + 32*hh .. +31] (e4m3 bytes)
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-        qreg[kk] = qi < Sq ? *(const h8*)(qb + (int64_t)qi * q_stride + 16 * kk + 8 * hh) : (h8){};
+        for (int kk = 0; kk < D / 64; ++kk) {
+            const uint8_t* src = qb + (int64_t)qi * q_stride + 64 * kk + 32 * hh;
+            const u4 lo = qi < Sq ? *(const u4*)src : (u4){};
+            const u4 hi = qi < Sq ? *(const u4*)(src + 16) : (u4){};
+            q8reg[kk] = (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            qreg[kk] = qi < Sq ? *(const h8*)((const _Float16*)qb + (int64_t)qi * q_stride + 16 * kk + 8 * hh)
+                               : (h8){};
+    }
+    // S^T for the 32-key sub-tile at row0 of the staged K tile
+    auto qk_sub = [&](const _Float16* Ks, int row0) __attribute__((always_inline)) {
+        if constexpr (FP8)
+            return qk_subtile_f8<D>((const uint8_t*)Ks, row0, q8reg, n, hh);
+        else
+            return qk_subtile_sw<D>(Ks, row0, qreg, n, hh);
+    };
 
     RowState st;
     f16v acc[DT];
@@ -179,11 +206,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const _Float16* Vs = Vst + ((j - 1) & 1) * tile_halves<D>();
         const _Float16* Ks = Kst + (j & 1) * tile_halves<D>();
         if (pv && qk) {
-            S[0] = qk_subtile_sw<D>(Ks, 0, qreg, n, hh);
-            S[1] = qk_subtile_sw<D>(Ks, 32, qreg, n, hh);
+            S[0] = qk_sub(Ks, 0);
+            S[1] = qk_sub(Ks, 32);
             softmax_exp<2, NAIVE>(P, st, apend);
             pv_chunks_tr<D, 4>(Vs, 0, P, acc, lane);
-            constexpr int NQK = 2 * (D / 16);   // one K read each
+            constexpr int NQK = FP8 ? 4 * (D / 64) : 2 * (D / 16);   // K reads; one product each
+                                                                   // (fp8: two reads per product)
             constexpr int NPV = 4 * (D / 32);   // two V reads each
             constexpr int AHEAD = 8;
             __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
@@ -203,8 +231,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 pv_chunks_tr<D, 4>(Vs, 0, P, acc, lane);
             }
             if (qk) {
-                S[0] = qk_subtile_sw<D>(Ks, 0, qreg, n, hh);
-                S[1] = qk_subtile_sw<D>(Ks, 32, qreg, n, hh);
+                S[0] = qk_sub(Ks, 0);
+                S[1] = qk_sub(Ks, 32);
             }
         }
         __builtin_amdgcn_s_setprio(0);
@@ -283,7 +311,7 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(kern, dim3((unsigned)n_items), dim3(kThreads), smem, stream,
                        (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
                        (_Float16*)a.o, a.lse, a.batch, a.seqlen_q, a.seqlen_kv, a.num_heads_q,
-                       a.gqa_group, a.softmax_scale * kLog2e, n_qtiles);
+                       a.gqa_group, a.softmax_scale * a.qk_dequant * kLog2e, n_qtiles);
     return hipGetLastError();
 }
 
@@ -293,6 +321,8 @@ hipError_t launch_var(const FwdArgs& a, int variant, hipStream_t stream) {
         return a.causal ? launch_one<D, true, kVarNaive>(a, stream) : launch_one<D, false, kVarNaive>(a, stream);
     if (variant == kVarStrict)
         return a.causal ? launch_one<D, true, kVarStrict>(a, stream) : launch_one<D, false, kVarStrict>(a, stream);
+    if (variant == kVarFp8)
+        return a.causal ? launch_one<D, true, kVarFp8>(a, stream) : launch_one<D, false, kVarFp8>(a, stream);
     return a.causal ? launch_one<D, true, kVarPasa>(a, stream) : launch_one<D, false, kVarPasa>(a, stream);
 }
 

@@ -272,6 +272,66 @@ __device__ __forceinline__ void stage_tile(i32x4 rsrc, uint32_t stride_b, int ro
     }
 }
 
+// ---------------------------------------------------------------------------
+// fp8 (e4m3) K tiles: ROWS rows x D one-byte columns.  Row r's 16-byte chunk c
+// lives at chunk slot r*C8 + (c ^ swz_f8(r)), C8 = D/16; rows that share a
+// bank window (their byte offsets are equal modulo 256) get distinct chunk
+// positions, so 16 lanes reading one chunk of 16 consecutive rows touch all
+// 64 banks once.
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+template <int D>
+__device__ __forceinline__ int swz_f8(int r) {
+    constexpr int C8 = D / 16;
+    return (r / (256 / D)) % C8;
+}
+
+template <int D, int ROWS, int WAVES>
+__device__ __forceinline__ void stage_tile_f8(i32x4 rsrc, uint32_t stride_b, int row0,
+                                              uint8_t* tile, int w, int lane) {
+    constexpr int C8 = D / 16;
+    constexpr int SEGS = ROWS * C8 / 64;         // 1 KB segments in the tile
+    static_assert(SEGS % WAVES == 0 || WAVES % SEGS == 0, "segments must split evenly");
+    constexpr int PER = SEGS >= WAVES ? SEGS / WAVES : 1;   // with fewer segments than
+    if (SEGS < WAVES && w >= SEGS) return;                  // waves, one each
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int seg = w * PER + i;
+        const int slot = seg * 64 + lane;
+        const int row = slot / C8, pos = slot % C8;
+        const int chunk = pos ^ swz_f8<D>(row);
+        const uint32_t off = (uint32_t)(row0 + row) * stride_b + (uint32_t)chunk * 16u;
+        dma16(rsrc, off, tile + seg * 1024);
+    }
+}
+
+// S^T (32 keys x 32 query columns) from an fp8 K tile and fp8 Q registers on
+// the fp8 matrix cores (v_mfma_f32_32x32x64_f8f6f4, both operands e4m3,
+// fp32 accumulate).  For contraction chunk kk (64 head-dim columns) lane
+// (n, g = lane / 32) supplies columns 64*kk + 32*g .. +31 of its K row (A)
+// and of its query row (B); A and B use the same assignment, so the products
+// pair matching columns.
+template <int D>
+__device__ __forceinline__ f16v qk_subtile_f8(const uint8_t* Ks, int row0, const v8i (&q8)[D / 64],
+                                              int n, int hh) {
+    constexpr int C8 = D / 16;
+    f16v s = (f16v){};
+    const int row = row0 + sigma(n);
+    const uint8_t* base = Ks + row * D;
+    const int sw = swz_f8<D>(row);
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk) {
+        const int c0 = 4 * kk + 2 * hh;
+        const u4 lo = *(const u4*)(base + 16 * ((c0) ^ sw));
+        const u4 hi = *(const u4*)(base + 16 * ((c0 + 1) ^ sw));
+        const v8i a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                       (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q8[kk], s, 0, 0, 0, 0, 0, 0);
+    }
+    (void)C8;
+    return s;
+}
+
 // s_waitcnt immediate for "at most n vector-memory operations outstanding"
 // (expcnt and lgkmcnt left at their maxima; vmcnt is split over bits 3:0
 // and 15:14).

@@ -28,7 +28,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared()
-    for fn in ("pasa_attn_fwd", "pasa_attn_fwd_strict", "pasa_naive_attn_fwd", "pasa_attn_decode",
+    for fn in ("pasa_attn_fwd", "pasa_attn_fwd_strict", "pasa_attn_fwd_fp8", "pasa_naive_attn_fwd",
+               "pasa_attn_decode",
                "pasa_attn_decode_paged",
                "pasa_attn_decode_combine", "pasa_attn_decode_workspace_bytes",
                "pasa_attn_decode_splits", "pasa_status_string"):
@@ -102,3 +103,18 @@ def test_status_strings(lib):
     texts = {lib.pasa_status_string(s) for s in (0, -1, -2, -3, -4)}
     assert len(texts) == 5
     assert lib.pasa_status_string(17) == b"unknown status"
+
+
+def test_fp8_fwd_validation(lib):
+    f = lib.pasa_attn_fwd_fp8
+    f.restype = ctypes.c_int
+
+    def call(q=P, k=P, v=P, o=P, B=1, D=64, qs=1.0, ks=1.0, causal=0):
+        return f(q, k, v, o, None, B, 8, 8, 2, 1, D, ctypes.c_float(0.125), ctypes.c_float(qs),
+                 ctypes.c_float(ks), causal, None)
+    assert call(q=None) == -1
+    assert call(B=0) == -1
+    assert call(D=96) == -2
+    assert call(qs=0.0) == -2
+    assert call(ks=-1.0) == -2
+    assert call(qs=float("inf")) == -2

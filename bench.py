@@ -36,7 +36,7 @@ CSRC = os.path.join(ROOT, "precision_flashattention_numerics_amd", "csrc")
 K_PREFILL = "fwd_kernelILi128ELb1ELi0E"      # PASA prefill, head_dim 128, causal
 K_STRICT = "fwd_kernelILi128ELb1ELi1E"       # strict PASA prefill, same shape
 K_NAIVE = "fwd_kernelILi128ELb1ELi2E"        # naive fp16 prefill, same shape
-K_SPLIT = "decode_split_kernelILi128E"       # decode split, head_dim 128
+K_SPLIT = "decode_split_kernelILi128ELb0E"   # decode split, head_dim 128, contiguous cache
 K_COMBINE = "decode_combine_kernel"
 
 PROFILE_CMDS = {

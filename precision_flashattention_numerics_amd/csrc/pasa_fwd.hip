@@ -48,13 +48,17 @@ namespace pasa {
 namespace {
 
 constexpr int kBR = 256;      // query rows per workgroup (32 per wave)
-constexpr int kBC = 64;       // keys per block
+// keys per block: 64 at head_dim 128, 128 at head_dim 64 (the same K/V tile
+// bytes; at head_dim 64 the matrix work per key halves, so the longer block
+// spreads the per-block vector work over more keys)
+template <int D>
+constexpr int kBCof() { return D == 64 ? 128 : 64; }
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;      // XCDs of an MI355X; workgroups are dealt round-robin
 
 template <int D>
-constexpr int tile_halves() { return kBC * D; }
+constexpr int tile_halves() { return kBCof<D>() * D; }
 template <int D>
 constexpr int fwd_smem_bytes() { return 2 /*stages*/ * 2 /*K,V*/ * tile_halves<D>() * 2; }
 
@@ -99,6 +103,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr int EB = FP8 ? 1 : 2;            // bytes per q / k element
     constexpr int KK = D / 16;
     constexpr int DT = D / 32;
+    constexpr int kBC = kBCof<D>();
+    constexpr int NT = kBC / 32;               // 32-key sub-tiles per block
     extern __shared__ __attribute__((aligned(1024))) _Float16 smem[];
 
     const int tid = threadIdx.x;
@@ -191,8 +197,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     f16v acc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[dt] = (f16v){};
-    f16v S[2];
-    h2 P[16];              // exponent arguments X of a block, then its P in place
+    f16v S[NT];
+    h2 P[8 * NT];          // exponent arguments X of a block, then its P in place
     _Float16 apend = 1;    // alpha of the block whose X is held in P
 
     // matrix phase of block j: S^T = K Q^T for block j with the exponentials
@@ -206,13 +212,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const _Float16* Vs = Vst + ((j - 1) & 1) * tile_halves<D>();
         const _Float16* Ks = Kst + (j & 1) * tile_halves<D>();
         if (pv && qk) {
-            S[0] = qk_sub(Ks, 0);
-            S[1] = qk_sub(Ks, 32);
-            softmax_exp<2, NAIVE>(P, st, apend);
-            pv_chunks_tr<D, 4>(Vs, 0, P, acc, lane);
-            constexpr int NQK = FP8 ? 4 * (D / 64) : 2 * (D / 16);   // K reads; one product each
-                                                                   // (fp8: two reads per product)
-            constexpr int NPV = 4 * (D / 32);   // two V reads each
+#pragma unroll
+            for (int t = 0; t < NT; ++t) S[t] = qk_sub(Ks, 32 * t);
+            softmax_exp<NT, NAIVE>(P, st, apend);
+            pv_chunks_tr<D, 2 * NT>(Vs, 0, P, acc, lane);
+            constexpr int NQK = FP8 ? 2 * NT * (D / 64) : NT * (D / 16);   // K reads; one product
+                                                                           // each (fp8: two reads)
+            constexpr int NPV = 2 * NT * (D / 32);   // two V reads each
             constexpr int AHEAD = 8;
             __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
@@ -227,12 +233,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         } else {
             if (pv) {
-                softmax_exp<2, NAIVE>(P, st, apend);
-                pv_chunks_tr<D, 4>(Vs, 0, P, acc, lane);
+                softmax_exp<NT, NAIVE>(P, st, apend);
+                pv_chunks_tr<D, 2 * NT>(Vs, 0, P, acc, lane);
             }
             if (qk) {
-                S[0] = qk_sub(Ks, 0);
-                S[1] = qk_sub(Ks, 32);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) S[t] = qk_sub(Ks, 32 * t);
             }
         }
         __builtin_amdgcn_s_setprio(0);
@@ -245,12 +251,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         _Float16 d;
         if (kbase + kBC <= wave_lim_lo) {   // the whole block is visible to the wave
             auto all = [](int, int) { return true; };
-            d = softmax_tile<2, NAIVE, decltype(all), STRICT>(S, P, st, c, true, kBC, all);
+            d = softmax_tile<NT, NAIVE, decltype(all), STRICT>(S, P, st, c, true, kBC, all);
         } else {
             const int m = lim - kbase;        // keys [0, m) of the block are visible
             const int cnt = max(0, min(kBC, m));
             auto vis = [&](int t, int r) { return 32 * t + key_of(r, hh) < m; };
-            d = softmax_tile<2, NAIVE, decltype(vis), STRICT>(S, P, st, c, false, cnt, vis);
+            d = softmax_tile<NT, NAIVE, decltype(vis), STRICT>(S, P, st, c, false, cnt, vis);
         }
         apend = hexp2(d);
         if (wave_any(apend != (_Float16)1)) {

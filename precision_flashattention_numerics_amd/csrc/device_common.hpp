@@ -33,9 +33,18 @@ __device__ __forceinline__ float xsum32(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// max of three floats in one instruction; no NaN canonicalisation of the
+// inputs (the kernels feed it finite scores and -inf)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
 __device__ __forceinline__ float xmax32(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    float m;
+    asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+    return m;
 }
 __device__ __forceinline__ _Float16 xsum32(_Float16 x) {
     const unsigned u = __builtin_bit_cast(unsigned short, x);
@@ -66,24 +75,24 @@ __device__ __forceinline__ h2 hexp2(h2 x) {
 
 __device__ __forceinline__ h2 hmax(h2 a, h2 b) { return __builtin_elementwise_max(a, b); }
 
-// exp2 of both halves of four packed pairs, written in place (no repacking):
-// v_exp_f16 on the low halves, then its SDWA form on the high halves, which
-// preserves the low result.  The preserving write reads the register a
-// transcendental instruction just wrote, a read that needs wait states on
-// this ISA; issuing the four low halves first puts three instructions
-// between each pair, and the trailing s_nop covers the first consumer.
-__device__ __forceinline__ void hexp2_pk4(const h2* x, h2* r) {
-    asm("v_exp_f16_e32 %0, %4\n\t"
-        "v_exp_f16_e32 %1, %5\n\t"
-        "v_exp_f16_e32 %2, %6\n\t"
-        "v_exp_f16_e32 %3, %7\n\t"
-        "v_exp_f16_sdwa %0, %4 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
-        "v_exp_f16_sdwa %1, %5 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
-        "v_exp_f16_sdwa %2, %6 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
-        "v_exp_f16_sdwa %3, %7 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
+// exp2 of both halves of four packed pairs, in place (same registers, no
+// repacking): the SDWA form of v_exp_f16 on the low halves, preserving the
+// high halves, then on the high halves, preserving the low results.  A
+// preserving write reads the register a transcendental instruction just
+// wrote, a read that needs wait states on this ISA; issuing the four low
+// halves first puts three instructions between each pair, and the trailing
+// s_nop covers the first consumer.
+__device__ __forceinline__ void hexp2_pk4(h2* r) {
+    asm("v_exp_f16_sdwa %0, %0 dst_sel:WORD_0 dst_unused:UNUSED_PRESERVE src0_sel:WORD_0\n\t"
+        "v_exp_f16_sdwa %1, %1 dst_sel:WORD_0 dst_unused:UNUSED_PRESERVE src0_sel:WORD_0\n\t"
+        "v_exp_f16_sdwa %2, %2 dst_sel:WORD_0 dst_unused:UNUSED_PRESERVE src0_sel:WORD_0\n\t"
+        "v_exp_f16_sdwa %3, %3 dst_sel:WORD_0 dst_unused:UNUSED_PRESERVE src0_sel:WORD_0\n\t"
+        "v_exp_f16_sdwa %0, %0 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
+        "v_exp_f16_sdwa %1, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
+        "v_exp_f16_sdwa %2, %2 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
+        "v_exp_f16_sdwa %3, %3 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
         "s_nop 1"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-        : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+        : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
 }
 
 // fp16(c * a + z) for two fp32 values, one rounding each (fused multiply-add

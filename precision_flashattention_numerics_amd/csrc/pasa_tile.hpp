@@ -105,19 +105,42 @@ __device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 
     _Float16 mb;
     float off = 0.0f;
     if (!NAIVE) {
-        // four independent partial sums / maxima keep the dependency chains short
-        float ps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        float pm[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+        // four independent partial sums / maxima keep the dependency chains
+        // short; each starts from the sub-tile's first scores
+        float ps[4], pm[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool on = full || vis(0, r);
+            ps[r] = on ? S[0][r] : 0.0f;
+            pm[r] = on ? S[0][r] : -__builtin_inff();
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int r = (t == 0 ? 4 : 0); r < 16; ++r) {
                 const bool on = full || vis(t, r);
                 ps[r & 3] += on ? S[t][r] : 0.0f;
-                pm[r & 3] = fmaxf(pm[r & 3], on ? S[t][r] : -__builtin_inff());
             }
+        // maxima two scores at a time (v_max3_f32 on the raw products: no
+        // NaN canonicalisation is needed for them)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            constexpr int NV = 4 * NT - 1;        // chain k: scores r = k mod 4 past the first
+            float vv[NV];
+            int nv = 0;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = k; r < 16; r += 4) {
+                    if (t == 0 && r == k) continue;
+                    vv[nv++] = (full || vis(t, r)) ? S[t][r] : -__builtin_inff();
+                }
+#pragma unroll
+            for (int i = 0; i + 1 < NV; i += 2) pm[k] = max3f(pm[k], vv[i], vv[i + 1]);
+            if (NV & 1) pm[k] = max3f(pm[k], vv[NV - 1], vv[NV - 1]);
+        }
         const float sum = xsum32((ps[0] + ps[1]) + (ps[2] + ps[3]));
-        const float m32 = xmax32(fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3])));
+        const float m32 = xmax32(max3f(pm[0], pm[1], max3f(pm[2], pm[3], pm[3])));
         const float cmu = cnt > 0 ? r16(c * (sum / (float)cnt)) : st.R;
         off = (st.R == -__builtin_inff()) ? cmu : fmaxf(cmu, st.R);
         mb = fma_to_h(m32, c, -off);
@@ -171,7 +194,7 @@ __device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 
 template <int NT, bool NAIVE>
 __device__ __forceinline__ void softmax_exp(h2 (&P)[8 * NT], RowState& st, _Float16 alpha) {
 #pragma unroll
-    for (int i = 0; i < 8 * NT; i += 4) hexp2_pk4(P + i, P + i);
+    for (int i = 0; i < 8 * NT; i += 4) hexp2_pk4(P + i);
 
     // fp16 pairwise tree sum of the lane's exponentials, then across halves
     h2 a[4 * NT];

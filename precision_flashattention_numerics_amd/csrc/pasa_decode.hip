@@ -109,12 +109,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
             const int64_t base = ((int64_t)(ok ? page : 0) * pg.page_size + key0 % pg.page_size) *
                                      kv_stride + (int64_t)hkv * D;
             const uint32_t bytes = ok ? (uint32_t)(((int64_t)(rows - 1) * kv_stride + D) * 2) : 0u;
-            stage_tile<D, kSub, 1, false>(make_rsrc(k + base, bytes), stride_b, 0, sk, 0, lane);
-            stage_tile<D, kSub, 1, true>(make_rsrc(v + base, bytes), stride_b, 0,
+            stage_tile<D, kSub, 1, false, true>(make_rsrc(k + base, bytes), stride_b, 0, sk, 0, lane);
+            stage_tile<D, kSub, 1, true, true>(make_rsrc(v + base, bytes), stride_b, 0,
                                          sk + sub_halves<D>(), 0, lane);
         } else {
-            stage_tile<D, kSub, 1, false>(krs, stride_b, key0, sk, 0, lane);
-            stage_tile<D, kSub, 1, true>(vrs, stride_b, key0, sk + sub_halves<D>(), 0, lane);
+            stage_tile<D, kSub, 1, false, true>(krs, stride_b, key0, sk, 0, lane);
+            stage_tile<D, kSub, 1, true, true>(vrs, stride_b, key0, sk + sub_halves<D>(), 0, lane);
         }
     };
 

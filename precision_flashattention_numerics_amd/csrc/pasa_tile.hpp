@@ -251,13 +251,23 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 // would otherwise wait for every such load before any later LDS read (it
 // cannot tell the staging buffers apart); this kernel orders them itself with
 // an explicit vmcnt(0) wait and a barrier before the tile is consumed.
+// STREAM marks the load non-temporal (nt): for data read exactly once (the
+// decode KV cache), which streams from HBM markedly faster that way; tiles
+// that other workgroups re-read through L2 (prefill K/V) keep the default.
+template <bool STREAM = false>
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, const void* lds) {
     const uint32_t la = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :
-                 : "v"(voff), "s"(rsrc), "s"(la)
-                 : "memory", "m0");
+    if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                     :
+                     : "v"(voff), "s"(rsrc), "s"(la)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"(voff), "s"(rsrc), "s"(la)
+                     : "memory", "m0");
 }
 
 template <int D>
@@ -277,8 +287,8 @@ typedef __attribute__((address_space(3))) s4 lds_s4;
 
 // Issue the loads of keys [row0, row0 + ROWS) of one head's K or V slab into
 // an LDS tile; the WAVES waves of the workgroup split the 1 KB segments.
-// stride_b = bytes between consecutive keys of the slab.
-template <int D, int ROWS, int WAVES, bool IS_V>
+// stride_b = bytes between consecutive keys of the slab; STREAM as in dma16.
+template <int D, int ROWS, int WAVES, bool IS_V, bool STREAM = false>
 __device__ __forceinline__ void stage_tile(i32x4 rsrc, uint32_t stride_b, int row0,
                                            _Float16* tile, int w, int lane) {
     constexpr int C = D / 8;
@@ -291,7 +301,7 @@ __device__ __forceinline__ void stage_tile(i32x4 rsrc, uint32_t stride_b, int ro
         const int row = slot / C, pos = slot % C;
         const int chunk = pos ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
         const uint32_t off = (uint32_t)(row0 + row) * stride_b + (uint32_t)chunk * 16u;
-        dma16(rsrc, off, tile + seg * 512);
+        dma16<STREAM>(rsrc, off, tile + seg * 512);
     }
 }
 

@@ -185,27 +185,48 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     }
 }
 
+// Up to kFast splits per row are combined from registers: every partial of
+// the row (its lse and this thread's o column) is loaded in one round of
+// independent loads before any arithmetic; more splits take the general loop.
+constexpr int kFast = 8;
+
 __global__ __launch_bounds__(128) void decode_combine_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part,
     _Float16* __restrict__ o, float* __restrict__ lse, int D, int nsplit) {
     const int64_t row = blockIdx.x;   // b * Hq + hq
     const float* lp = lse_part + row * nsplit;
-    float M = -__builtin_inff();
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lp[s]);
-    float sum = 0.0f;
-    if (M != -__builtin_inff())
-        for (int s = 0; s < nsplit; ++s) sum += expf(lp[s] - M);
-    const float L = M != -__builtin_inff() ? M + logf(sum) : -__builtin_inff();
+    const float* op = o_part + row * nsplit * D;
     const int d = threadIdx.x;
-    if (d < D) {
-        float val = 0.0f;
+    const bool col = d < D;
+    float M = -__builtin_inff(), L, val = 0.0f;
+    if (nsplit <= kFast) {
+        float lv[kFast], ov[kFast];
+#pragma unroll
+        for (int s = 0; s < kFast; ++s) {
+            lv[s] = s < nsplit ? lp[s] : -__builtin_inff();
+            ov[s] = (s < nsplit && col) ? op[s * D + d] : 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < kFast; ++s) M = fmaxf(M, lv[s]);
+        float sum = 0.0f;
         if (M != -__builtin_inff())
-            for (int s = 0; s < nsplit; ++s) {
-                const float wgt = expf(lp[s] - L);
-                val += wgt * o_part[(row * nsplit + s) * D + d];
-            }
-        o[row * D + d] = (_Float16)val;
+#pragma unroll
+            for (int s = 0; s < kFast; ++s) sum += s < nsplit ? expf(lv[s] - M) : 0.0f;
+        L = M != -__builtin_inff() ? M + logf(sum) : -__builtin_inff();
+        if (M != -__builtin_inff())
+#pragma unroll
+            for (int s = 0; s < kFast; ++s)
+                if (s < nsplit) val += expf(lv[s] - L) * ov[s];
+    } else {
+        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lp[s]);
+        float sum = 0.0f;
+        if (M != -__builtin_inff())
+            for (int s = 0; s < nsplit; ++s) sum += expf(lp[s] - M);
+        L = M != -__builtin_inff() ? M + logf(sum) : -__builtin_inff();
+        if (M != -__builtin_inff() && col)
+            for (int s = 0; s < nsplit; ++s) val += expf(lp[s] - L) * op[s * D + d];
     }
+    if (col) o[row * D + d] = (_Float16)val;
     if (lse != nullptr && d == 0) lse[row] = L;
 }
 

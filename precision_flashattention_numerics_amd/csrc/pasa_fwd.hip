@@ -152,17 +152,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
     _Float16* const Kst = smem;                           // 2 stages of K
     _Float16* const Vst = smem + 2 * tile_halves<D>();    // 2 stages of V
+    // LDS DMA constants of this wave, and the stages' LDS byte addresses
+    const uint32_t w_u = __builtin_amdgcn_readfirstlane((uint32_t)w);
+    const TileDma<D, kBC, kWaves, false> kdma(stride_b, w_u, lane);
+    const TileDma<D, kBC, kWaves, true> vdma(stride_b, w_u, lane);
+    constexpr uint32_t kTileBytes = tile_halves<D>() * 2;
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
+    const uint32_t k_bytes = (uint32_t)(((int64_t)(Skv - 1) * kv_stride + D) * EB);
     auto load_k = [&](int blk) {
-        if constexpr (FP8)
+        if constexpr (FP8) {
             stage_tile_f8<D, kBC, kWaves>(krs, (uint32_t)kv_stride, blk * kBC,
                                           (uint8_t*)(Kst + (blk & 1) * tile_halves<D>()), w, lane);
-        else
-            stage_tile<D, kBC, kWaves, false>(krs, stride_b, blk * kBC,
-                                              Kst + (blk & 1) * tile_halves<D>(), w, lane);
+        } else {
+            const uint32_t off = (uint32_t)(blk * kBC) * stride_b;   // < k_bytes (blk < nblocks)
+            kdma.issue(make_rsrc(kb + off, k_bytes - off), smem_lds + (blk & 1) * kTileBytes);
+        }
     };
     auto load_v = [&](int blk) {
-        stage_tile<D, kBC, kWaves, true>(vrs, stride_b, blk * kBC,
-                                         Vst + (blk & 1) * tile_halves<D>(), w, lane);
+        const uint32_t off = (uint32_t)(blk * kBC) * stride_b;
+        vdma.issue(make_rsrc((const uint8_t*)vb + off, slab_bytes - off),
+                   smem_lds + (2 + (blk & 1)) * kTileBytes);
     };
     if (nblocks > 0) load_k(0);
 

@@ -305,6 +305,43 @@ __device__ __forceinline__ void stage_tile(i32x4 rsrc, uint32_t stride_b, int ro
     }
 }
 
+// The same staging with everything that does not change from one key block
+// to the next computed once, outside the key loop: each lane's byte offset
+// inside a block (row, swizzled chunk) and each of this wave's segments' LDS
+// byte offset inside a stage.  Per block the caller passes a descriptor that
+// starts at the block's first key (bounded by the slab end, so rows past the
+// sequence read as zero) and the stage's LDS byte address; issuing a segment
+// is then scalar moves and one load.  w_u is the wave index, wave-uniform.
+template <int D, int ROWS, int WAVES, bool IS_V>
+struct TileDma {
+    static constexpr int C = D / 8;
+    static constexpr int SEGS = ROWS * C / 64;   // 1 KB segments in the tile
+    static constexpr int PER = SEGS / WAVES;
+    static_assert(SEGS % WAVES == 0, "segments must split evenly over waves");
+    uint32_t voff[PER];   // per lane: bytes from the block's first key
+    uint32_t lds[PER];    // per wave: bytes from the stage's start
+
+    __device__ __forceinline__ TileDma(uint32_t stride_b, uint32_t w_u, int lane) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int seg = (int)w_u * PER + i;
+            const int slot = seg * 64 + lane;
+            const int row = slot / C, pos = slot % C;
+            const int chunk = pos ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
+            voff[i] = (uint32_t)row * stride_b + (uint32_t)chunk * 16u;
+            lds[i] = (uint32_t)seg * 1024u;
+        }
+    }
+    __device__ __forceinline__ void issue(i32x4 rsrc, uint32_t stage_lds) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :
+                         : "v"(voff[i]), "s"(rsrc), "s"(stage_lds + lds[i])
+                         : "memory", "m0");
+    }
+};
+
 // ---------------------------------------------------------------------------
 // fp8 (e4m3) K tiles: ROWS rows x D one-byte columns.  Row r's 16-byte chunk c
 // lives at chunk slot r*C8 + (c ^ swz_f8(r)), C8 = D/16; rows that share a

@@ -128,8 +128,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint8_t* kb = (const uint8_t*)k + ((int64_t)b * Skv * Hkv + hkv) * D * EB;
     const _Float16* vb = v + ((int64_t)b * Skv * Hkv + hkv) * D;
     const uint32_t slab_bytes = (uint32_t)(((int64_t)(Skv - 1) * kv_stride + D) * 2);
-    const i32x4 krs = make_rsrc(kb, (uint32_t)(((int64_t)(Skv - 1) * kv_stride + D) * EB));
-    const i32x4 vrs = make_rsrc(vb, slab_bytes);
     const uint32_t stride_b = (uint32_t)(kv_stride * 2);
 
     // ---- key range of this workgroup and of this lane's row
@@ -154,19 +152,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     _Float16* const Vst = smem + 2 * tile_halves<D>();    // 2 stages of V
     // LDS DMA constants of this wave, and the stages' LDS byte addresses
     const uint32_t w_u = __builtin_amdgcn_readfirstlane((uint32_t)w);
-    const TileDma<D, kBC, kWaves, false> kdma(stride_b, w_u, lane);
+    const TileDma<D, kBC, kWaves, false, FP8> kdma(FP8 ? (uint32_t)kv_stride : stride_b, w_u, lane);
     const TileDma<D, kBC, kWaves, true> vdma(stride_b, w_u, lane);
     constexpr uint32_t kTileBytes = tile_halves<D>() * 2;
     const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
     const uint32_t k_bytes = (uint32_t)(((int64_t)(Skv - 1) * kv_stride + D) * EB);
     auto load_k = [&](int blk) {
-        if constexpr (FP8) {
-            stage_tile_f8<D, kBC, kWaves>(krs, (uint32_t)kv_stride, blk * kBC,
-                                          (uint8_t*)(Kst + (blk & 1) * tile_halves<D>()), w, lane);
-        } else {
-            const uint32_t off = (uint32_t)(blk * kBC) * stride_b;   // < k_bytes (blk < nblocks)
-            kdma.issue(make_rsrc(kb + off, k_bytes - off), smem_lds + (blk & 1) * kTileBytes);
-        }
+        const uint32_t off = (uint32_t)(blk * kBC) * (uint32_t)(kv_stride * EB);   // < k_bytes
+        kdma.issue(make_rsrc(kb + off, k_bytes - off), smem_lds + (blk & 1) * kTileBytes);
     };
     auto load_v = [&](int blk) {
         const uint32_t off = (uint32_t)(blk * kBC) * stride_b;

@@ -305,43 +305,6 @@ __device__ __forceinline__ void stage_tile(i32x4 rsrc, uint32_t stride_b, int ro
     }
 }
 
-// The same staging with everything that does not change from one key block
-// to the next computed once, outside the key loop: each lane's byte offset
-// inside a block (row, swizzled chunk) and each of this wave's segments' LDS
-// byte offset inside a stage.  Per block the caller passes a descriptor that
-// starts at the block's first key (bounded by the slab end, so rows past the
-// sequence read as zero) and the stage's LDS byte address; issuing a segment
-// is then scalar moves and one load.  w_u is the wave index, wave-uniform.
-template <int D, int ROWS, int WAVES, bool IS_V>
-struct TileDma {
-    static constexpr int C = D / 8;
-    static constexpr int SEGS = ROWS * C / 64;   // 1 KB segments in the tile
-    static constexpr int PER = SEGS / WAVES;
-    static_assert(SEGS % WAVES == 0, "segments must split evenly over waves");
-    uint32_t voff[PER];   // per lane: bytes from the block's first key
-    uint32_t lds[PER];    // per wave: bytes from the stage's start
-
-    __device__ __forceinline__ TileDma(uint32_t stride_b, uint32_t w_u, int lane) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int seg = (int)w_u * PER + i;
-            const int slot = seg * 64 + lane;
-            const int row = slot / C, pos = slot % C;
-            const int chunk = pos ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
-            voff[i] = (uint32_t)row * stride_b + (uint32_t)chunk * 16u;
-            lds[i] = (uint32_t)seg * 1024u;
-        }
-    }
-    __device__ __forceinline__ void issue(i32x4 rsrc, uint32_t stage_lds) const {
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-            asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                         :
-                         : "v"(voff[i]), "s"(rsrc), "s"(stage_lds + lds[i])
-                         : "memory", "m0");
-    }
-};
-
 // ---------------------------------------------------------------------------
 // fp8 (e4m3) K tiles: ROWS rows x D one-byte columns.  Row r's 16-byte chunk c
 // lives at chunk slot r*C8 + (c ^ swz_f8(r)), C8 = D/16; rows that share a
@@ -356,24 +319,44 @@ __device__ __forceinline__ int swz_f8(int r) {
     return (r / (256 / D)) % C8;
 }
 
-template <int D, int ROWS, int WAVES>
-__device__ __forceinline__ void stage_tile_f8(i32x4 rsrc, uint32_t stride_b, int row0,
-                                              uint8_t* tile, int w, int lane) {
-    constexpr int C8 = D / 16;
-    constexpr int SEGS = ROWS * C8 / 64;         // 1 KB segments in the tile
-    static_assert(SEGS % WAVES == 0 || WAVES % SEGS == 0, "segments must split evenly");
-    constexpr int PER = SEGS >= WAVES ? SEGS / WAVES : 1;   // with fewer segments than
-    if (SEGS < WAVES && w >= SEGS) return;                  // waves, one each
+// The staging of stage_tile with everything that does not change from one key block
+// to the next computed once, outside the key loop: each lane's byte offset
+// inside a block (row, swizzled chunk) and each of this wave's segments' LDS
+// byte offset inside a stage.  Per block the caller passes a descriptor that
+// starts at the block's first key (bounded by the slab end, so rows past the
+// sequence read as zero) and the stage's LDS byte address; issuing a segment
+// is then scalar moves and one load.  w_u is the wave index, wave-uniform.
+// F8: one-byte (e4m3) K tile in the fp8 layout above.
+template <int D, int ROWS, int WAVES, bool IS_V, bool F8 = false>
+struct TileDma {
+    static constexpr int C = F8 ? D / 16 : D / 8;   // 16-byte chunks per row
+    static constexpr int SEGS = ROWS * C / 64;   // 1 KB segments in the tile
+    static constexpr int PER = SEGS / WAVES;
+    static_assert(SEGS % WAVES == 0, "segments must split evenly over waves");
+    uint32_t voff[PER];   // per lane: bytes from the block's first key
+    uint32_t lds[PER];    // per wave: bytes from the stage's start
+
+    __device__ __forceinline__ TileDma(uint32_t stride_b, uint32_t w_u, int lane) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int seg = w * PER + i;
-        const int slot = seg * 64 + lane;
-        const int row = slot / C8, pos = slot % C8;
-        const int chunk = pos ^ swz_f8<D>(row);
-        const uint32_t off = (uint32_t)(row0 + row) * stride_b + (uint32_t)chunk * 16u;
-        dma16(rsrc, off, tile + seg * 1024);
+        for (int i = 0; i < PER; ++i) {
+            const int seg = (int)w_u * PER + i;
+            const int slot = seg * 64 + lane;
+            const int row = slot / C, pos = slot % C;
+            const int chunk = pos ^ (F8 ? swz_f8<D>(row) : IS_V ? swz_v<D>(row) : swz_k<D>(row));
+            voff[i] = (uint32_t)row * stride_b + (uint32_t)chunk * 16u;
+            lds[i] = (uint32_t)seg * 1024u;
+        }
     }
-}
+    __device__ __forceinline__ void issue(i32x4 rsrc, uint32_t stage_lds) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                         :
+                         : "v"(voff[i]), "s"(rsrc), "s"(stage_lds + lds[i])
+                         : "memory", "m0");
+    }
+};
+
 
 // S^T (32 keys x 32 query columns) from an fp8 K tile and fp8 Q registers on
 // the fp8 matrix cores (v_mfma_f32_32x32x64_f8f6f4, both operands e4m3,

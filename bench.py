@@ -8,7 +8,11 @@ One step = the whole hot path over one batch of synthetic input:
 `value` is the prefill's TFLOP/s over algorithmic flops (4 * head_dim per
 visible query/key pair), from HIP events recorded on the launch stream around
 each prefill call inside the timed steps; the decode's achieved HBM GB/s is
-reported beside it.  Inputs are resident in HBM before timing starts.
+reported beside it.  Inputs are resident in HBM before timing starts, and
+the timed steps follow --warm-seconds of back-to-back warmup steps: the GPU
+raises its clock only after tens of milliseconds of sustained load, so a
+burst timed right after an idle spell measures the clock ramp instead of the
+kernel (that cold figure is reported beside it as prefill_ms_cold).
 
 Also reported: relative RMSE of sampled output rows against the binary64
 oracle, the naive fp16 kernel's inf/NaN count on the same input (the overflow
@@ -43,20 +47,20 @@ PROFILE_CMDS = {
     "trace": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/trace -o run --output-format csv "
              "-- python bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-other-configs",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/fetch -o run --output-format csv "
-             "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-other-configs",
+             "-- python bench.py --steps 3 --warmup 1 --warm-seconds 0 --no-cpu-baseline --no-other-configs",
     "write": "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/write -o run --output-format csv "
-             "-- python bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-other-configs",
+             "-- python bench.py --steps 3 --warmup 1 --warm-seconds 0 --no-cpu-baseline --no-other-configs",
     "cfetch": "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/cfetch -o run --output-format csv "
               "-- python bench.py --calibrate-copy 1024",
     "cwrite": "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/cwrite -o run --output-format csv "
               "-- python bench.py --calibrate-copy 1024",
     "pmc1": "rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU "
             "SQ_INSTS_VMEM SQ_BUSY_CYCLES SQ_WAVE_CYCLES -d gpurun_out/prof/pmc1 -o run "
-            "--output-format csv -- python bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-other-configs",
+            "--output-format csv -- python bench.py --steps 3 --warmup 1 --warm-seconds 0 --no-cpu-baseline --no-other-configs",
     "pmc2": "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU "
             "SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_ACTIVE_INST_ANY SQ_WAIT_ANY GRBM_GUI_ACTIVE "
             "-d gpurun_out/prof/pmc2 -o run --output-format csv -- python bench.py --steps 3 "
-            "--warmup 1 --no-cpu-baseline --no-other-configs",
+            "--warmup 1 --warm-seconds 0 --no-cpu-baseline --no-other-configs",
 }
 
 
@@ -205,6 +209,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warm-seconds", type=float, default=0.3,
+                    help="keep running warmup steps until this much wall time has passed "
+                         "(the GPU clock ramps up over the first ~40 ms of sustained load)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing and the sampled parity check")
     ap.add_argument("--no-other-configs", action="store_true",
@@ -280,11 +287,35 @@ def main():
         pasa.attn_decode(tqd, tkd, tvd, scale=wd.scale, out=od, lse=ld, workspace=ws,
                          num_splits=nsplit)
 
-    log(f"warmup {args.warmup} steps ...")
-    for _ in range(args.warmup):
+    def warm(fn, seconds, min_iters=1):
+        """Run fn back to back until min_iters calls and `seconds` of wall time:
+        the GPU raises its clock only after tens of milliseconds of sustained
+        load, so timings taken right after an idle spell measure the ramp."""
+        t = time.perf_counter()
+        i = 0
+        while i < min_iters or time.perf_counter() - t < seconds:
+            for _ in range(8):
+                fn()
+            i += 8
+            torch.cuda.synchronize()
+        return i
+
+    def step():
         prefill()
         decode()
+
+    # the first prefill launches after the idle spell (clock not yet raised),
+    # reported beside the steady-state figure
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        prefill()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    cold_ms = e0.elapsed_time(e1) / 5
+    n_warm = warm(step, args.warm_seconds, args.warmup)
+    log(f"warmup {n_warm} steps ({args.warm_seconds} s) ...")
 
     # K steps: the K prefill launches back to back, then the K decode launches,
     # each run bracketed by events on the launch stream, so that a kernel's
@@ -325,13 +356,17 @@ def main():
     # the variant with fp16 running maximum and offset: its error is reported
     # beside the default's (and its speed, outside the timed steps)
     os_, ls_ = pasa.attn_fwd_strict(tqp, tkp, tvp, causal=wp.causal, scale=wp.scale)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
+
+    def strict():
         pasa.attn_fwd_strict(tqp, tkp, tvp, causal=wp.causal, scale=wp.scale, out=os_, lse=ls_)
-    e1.record()
+    warm(strict, 0.1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        strict()
+    e1.record(stream)
     torch.cuda.synchronize()
-    out["strict_tflops"] = round(flops / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e12, 3)
+    out["strict_tflops"] = round(flops / (e0.elapsed_time(e1) / K * 1e-3) / 1e12, 3)
     os_np, ls_np = os_.cpu().numpy(), ls_.cpu().numpy()
     out["strict_nonfinite"] = nonfinite(os_np)
 
@@ -339,22 +374,37 @@ def main():
     # (its latency is reported), c3 and c4 against the same MFMA peak
     if not args.no_other_configs:
         other = {}
-        for name, reps in (("c1", 20), ("c3", 10), ("c4", 3)):
+        for name, reps in (("c1", 20), ("c3", 10), ("c4", 2)):
             w = W.CONFIGS[name]
             log(f"config {name} ...")
             tq, tk, tv = (torch.from_numpy(x).cuda() for x in W.generate(w))
             o2 = torch.empty_like(tq)
             l2 = torch.empty((w.batch, w.heads_q, w.seqlen_q), dtype=torch.float32, device="cuda")
-            for _ in range(2):
+            def fwd2():
                 pasa.attn_fwd(tq, tk, tv, causal=w.causal, scale=w.scale, out=o2, lse=l2)
             ts = []
-            for _ in range(reps):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                pasa.attn_fwd(tq, tk, tv, causal=w.causal, scale=w.scale, out=o2, lse=l2)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1))
+            if name == "c1":
+                # launch-bound: the latency of single launches
+                for _ in range(2):
+                    fwd2()
+                for _ in range(reps):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    fwd2()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1))
+            else:
+                # throughput: warm, then batches of back-to-back launches
+                warm(fwd2, 0.15)
+                for _ in range(5):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for _ in range(reps):
+                        fwd2()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1) / reps)
             ts.sort()
             med = ts[len(ts) // 2]
             tf = w.flops() / (med * 1e-3) / 1e12
@@ -375,10 +425,14 @@ def main():
         table = perm.reshape(wd.batch, wd.seqlen_kv // ps).contiguous()
         lens = torch.full((wd.batch,), wd.seqlen_kv, dtype=torch.int32, device="cuda")
         opg, lpg = pasa.attn_decode_paged(tqd, kpool, vpool, table, lens, scale=wd.scale)
+
+        def paged():
+            pasa.attn_decode_paged(tqd, kpool, vpool, table, lens, scale=wd.scale, out=opg, lse=lpg)
+        warm(paged, 0.1)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(10):
-            pasa.attn_decode_paged(tqd, kpool, vpool, table, lens, scale=wd.scale, out=opg, lse=lpg)
+            paged()
         e1.record(stream)
         torch.cuda.synchronize()
         pg_ms = e0.elapsed_time(e1) / 10
@@ -394,10 +448,14 @@ def main():
         q8 = torch.clamp(tqp.float() / q8s, -448.0, 448.0).to(torch.float8_e4m3fn)
         k8 = torch.clamp(tkp.float() / k8s, -448.0, 448.0).to(torch.float8_e4m3fn)
         o8, l8 = pasa.attn_fwd_fp8(q8, k8, tvp, q8s, k8s, causal=wp.causal, scale=wp.scale)
+
+        def fp8():
+            pasa.attn_fwd_fp8(q8, k8, tvp, q8s, k8s, causal=wp.causal, scale=wp.scale, out=o8, lse=l8)
+        warm(fp8, 0.1)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(10):
-            pasa.attn_fwd_fp8(q8, k8, tvp, q8s, k8s, causal=wp.causal, scale=wp.scale, out=o8, lse=l8)
+            fp8()
         e1.record(stream)
         torch.cuda.synchronize()
         f8_ms = e0.elapsed_time(e1) / 10
@@ -462,6 +520,8 @@ def main():
                               "heads_kv": wd.heads_kv, "head_dim": wd.head_dim,
                               "splits": nsplit, "bias": 30}},
         "prefill_ms": round(pre_avg, 5),
+        "prefill_ms_cold": round(cold_ms, 5),
+        "warm_seconds": args.warm_seconds,
         "prefill_frac_of_peak": round(tflops / PEAK_FP16_TFLOPS, 4),
         "decode_ms": round(dec_avg, 5),
         "decode_GBps": round(dec_gbps, 1),

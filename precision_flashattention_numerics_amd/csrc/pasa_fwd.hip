@@ -105,6 +105,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     constexpr int DT = D / 32;
     constexpr int kBC = kBCof<D>();
     constexpr int NT = kBC / 32;               // 32-key sub-tiles per block
+    // packed pairs whose exponentials the vector phase takes (the matrix phase
+    // takes the rest): at head_dim 64 the matrix phase has half the products
+    // per score, so all of them go to the vector phase
+    constexpr int EV = D == 64 ? 8 * NT : 0;
     extern __shared__ __attribute__((aligned(1024))) _Float16 smem[];
 
     const int tid = threadIdx.x;
@@ -216,26 +220,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         if (pv && qk) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) S[t] = qk_sub(Ks, 32 * t);
-            softmax_exp<NT, NAIVE>(P, st, apend);
+            softmax_exp<NT, NAIVE, EV>(P, st, apend);
             pv_chunks_tr<D, 2 * NT>(Vs, 0, P, acc, lane);
-            constexpr int NQK = FP8 ? 2 * NT * (D / 64) : NT * (D / 16);   // K reads; one product
-                                                                           // each (fp8: two reads)
-            constexpr int NPV = 2 * NT * (D / 32);   // two V reads each
-            constexpr int AHEAD = 8;
-            __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+            // Operand reads are kept AHEADM products ahead of the product that
+            // consumes them, across the boundary between the two products: the
+            // V reads of the first P V products go out under the last S^T
+            // products
+            constexpr int NQKM = FP8 ? NT * (D / 64) : NT * (D / 16);   // S^T products
+            constexpr int RQ = FP8 ? 2 : 1;                             // K reads per S^T product
+            constexpr int NPV = 2 * NT * (D / 32);                      // P V products, 2 V reads each
+            constexpr int AHEADM = 8;
+            constexpr int FIRST = AHEADM <= NQKM ? AHEADM * RQ : NQKM * RQ + 2 * (AHEADM - NQKM);
+            __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
 #pragma unroll
-            for (int i = 0; i < NQK; ++i) {
+            for (int m = 0; m < NQKM + NPV; ++m) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < NPV; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (2 * i + AHEAD < 2 * NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                const int nx = m + AHEADM;   // product whose operands are read next
+                if (nx < NQKM) {
+                    if (RQ == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                } else if (nx < NQKM + NPV) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
             }
         } else {
             if (pv) {
-                softmax_exp<NT, NAIVE>(P, st, apend);
+                softmax_exp<NT, NAIVE, EV>(P, st, apend);
                 pv_chunks_tr<D, 2 * NT>(Vs, 0, P, acc, lane);
             }
             if (qk) {
@@ -261,6 +271,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             d = softmax_tile<NT, NAIVE, decltype(vis), STRICT>(S, P, st, c, false, cnt, vis);
         }
         apend = hexp2(d);
+        exp_pairs<0, EV>(P);
         if (wave_any(apend != (_Float16)1)) {
             const float af = (float)apend;
 #pragma unroll

@@ -191,10 +191,18 @@ __device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 
     return d;
 }
 
-template <int NT, bool NAIVE>
-__device__ __forceinline__ void softmax_exp(h2 (&P)[8 * NT], RowState& st, _Float16 alpha) {
+// P = exp2(X) in place for the packed pairs [FIRST, LAST) of a block
+// (multiples of 4).
+template <int FIRST, int LAST>
+__device__ __forceinline__ void exp_pairs(h2* P) {
 #pragma unroll
-    for (int i = 0; i < 8 * NT; i += 4) hexp2_pk4(P + i);
+    for (int i = FIRST; i < LAST; i += 4) hexp2_pk4(P + i);
+}
+
+// FIRST: pairs [0, FIRST) were already exponentiated by the caller.
+template <int NT, bool NAIVE, int FIRST = 0>
+__device__ __forceinline__ void softmax_exp(h2 (&P)[8 * NT], RowState& st, _Float16 alpha) {
+    exp_pairs<FIRST, 8 * NT>(P);
 
     // fp16 pairwise tree sum of the lane's exponentials, then across halves
     h2 a[4 * NT];

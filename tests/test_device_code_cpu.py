@@ -1,0 +1,93 @@
+"""Checks on the gfx950 assembly of the kernels (hipcc cross-compiles without a
+GPU): properties the sources rely on but the compiler could silently break.
+
+* no packed fp32 arithmetic (the build disables it; its results are not
+  trusted on this hardware),
+* no round-toward-zero fp16 conversion (every fp32 -> fp16 rounding in the
+  kernels is round-to-nearest-even),
+* no scalar-cache writes (scalar stores, scalar atomics, scalar cache
+  write-back or discard),
+* no scratch memory (register spills would put stack traffic in the loop),
+* M0 is written only by the kernels' own LDS-DMA sequences and read by nothing
+  else: those sequences set M0 in inline assembly, which is sound only while
+  the compiler keeps no value of its own in M0.
+"""
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+from precision_flashattention_numerics_amd import build as B  # noqa: E402
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+pytestmark = pytest.mark.skipif(shutil.which(HIPCC) is None, reason="hipcc not available")
+
+KERNEL_SOURCES = ("pasa_fwd.hip", "pasa_decode.hip")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = {}
+    d = tmp_path_factory.mktemp("asm")
+    flags = [f for f in B.FLAGS if f not in ("-shared", "-fPIC")]
+    for src in KERNEL_SOURCES:
+        path = os.path.join(B.CSRC, src)
+        dst = os.path.join(d, src + ".s")
+        subprocess.run([HIPCC, *flags, "-w", "--cuda-device-only", "-S", "-o", dst, path],
+                       check=True)
+        out[src] = [l.split(";")[0].strip() for l in open(dst)]
+    return out
+
+
+def instructions(lines):
+    return [l for l in lines if l and not l.startswith(".") and not l.endswith(":")]
+
+
+@pytest.mark.parametrize("src", KERNEL_SOURCES)
+def test_no_packed_fp32_math(asm, src):
+    bad = [l for l in instructions(asm[src]) if re.match(r"v_pk_(add|mul|fma)_f32\b", l)]
+    assert not bad, bad[:5]
+
+
+@pytest.mark.parametrize("src", KERNEL_SOURCES)
+def test_no_round_toward_zero_conversion(asm, src):
+    bad = [l for l in instructions(asm[src]) if l.startswith("v_cvt_pkrtz")]
+    assert not bad, bad[:5]
+
+
+@pytest.mark.parametrize("src", KERNEL_SOURCES)
+def test_no_scalar_cache_writes(asm, src):
+    pat = re.compile(r"s_(store|buffer_store|scratch_store|atomic|buffer_atomic|dcache_wb|dcache_discard)")
+    bad = [l for l in instructions(asm[src]) if pat.match(l)]
+    assert not bad, bad[:5]
+
+
+def test_no_scratch(asm):
+    for src in KERNEL_SOURCES:
+        text = "\n".join(asm[src])
+        sizes = re.findall(r"\.private_segment_fixed_size:\s*(\d+)", text)
+        assert sizes, src
+        assert all(int(x) == 0 for x in sizes), (src, sizes)
+
+
+@pytest.mark.parametrize("src", KERNEL_SOURCES)
+def test_m0_only_in_lds_dma(asm, src):
+    ins = instructions(asm[src])
+    n_dma = 0
+    for i, l in enumerate(ins):
+        if "m0" not in l:
+            continue
+        if l.startswith("s_mov_b32 m0,"):
+            # the next instruction past the s_nop is the LDS-DMA load that consumes it
+            nxt = [x for x in ins[i + 1:i + 3] if not x.startswith("s_nop")]
+            assert nxt and re.match(r"buffer_load_dword\w*\s.*\blds\b", nxt[0]), (l, ins[i + 1:i + 3])
+            n_dma += 1
+        else:
+            raise AssertionError(f"M0 used outside the LDS-DMA sequences: {l}")
+    assert n_dma > 0

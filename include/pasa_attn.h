@@ -63,8 +63,10 @@ typedef enum {
  *   causal    0 or 1 (bottom-right aligned).
  * Errors: PASA_ERR_INVALID for a null q/k/v/o, a size < 1, or
  * num_heads_q % gqa_group != 0; PASA_ERR_UNSUPPORTED for head_dim not in
- * {64,128}, seqlen_kv > 65504, a non-finite or non-positive softmax_scale, or
- * sizes whose element count overflows 64-bit indexing.
+ * {64,128}, seqlen_kv > 65504, a non-finite or non-positive softmax_scale,
+ * sizes whose element count overflows 64-bit indexing, or more than 2^31 - 1
+ * work items of 256 query rows of one head (batch * num_heads_q *
+ * ceil(seqlen_q / 256)).
  */
 int pasa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                   int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group,

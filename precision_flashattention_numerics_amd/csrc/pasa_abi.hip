@@ -51,6 +51,9 @@ int fwd_common(int variant, const void* q, const void* k, const void* v, void* o
     if (rc != PASA_OK) return rc;
     if (causal != 0 && causal != 1) return PASA_ERR_INVALID;
     if (seqlen_kv > kMaxFp16Sum) return PASA_ERR_UNSUPPORTED;
+    // the prefill's work items (256 query rows of one head) are counted in int
+    if ((int64_t)batch * num_heads_q * ((seqlen_q + 255) / 256) > 0x7FFFFFFFLL)
+        return PASA_ERR_UNSUPPORTED;
     pasa::FwdArgs a{q, k, v, o, lse, batch, seqlen_q, seqlen_kv, num_heads_q, gqa_group,
                     head_dim, softmax_scale, causal, qk_dequant};
     return pasa::launch_fwd(a, variant, stream) == hipSuccess ? PASA_OK : PASA_ERR_HIP;

@@ -64,6 +64,8 @@ def test_fwd_validation(lib, name):
     assert _fwd(lib, name, Skv=65505) == -2
     assert _fwd(lib, name, scale=0.0) == -2
     assert _fwd(lib, name, scale=float("nan")) == -2
+    # more 256-row work items than an int counts (the tensors would not fit a GPU)
+    assert _fwd(lib, name, B=65535, Sq=1, Skv=1, Hq=65535, g=65535) == -2
 
 
 def test_decode_validation_and_sizes(lib):

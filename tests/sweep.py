@@ -19,7 +19,14 @@ What a point reports
   naive_overflow   predicted: some unscaled score rounds to fp16 infinity
                    (|q.k| >= 65520, round-to-nearest-even)
   max_abs_cs       largest |scale * q.k * log2(e)| (the strict variant's range)
+  refine_rate      fraction of (row, key block) steps in which PASA's rule
+                   re-centres the fp16 tile at the row's own maximum, replayed
+                   in binary64 on the sampled rows (the kernels take the same
+                   decision in fp32, branch-free, and keep no count)
   <kernel>_nonfinite, <kernel>_rel_rmse   per kernel, on the sampled rows
+
+`python -m tests.sweep --replay-only [--full]` computes only the columns that
+need no GPU (scores, predicted overflow, refine rate).
 """
 import argparse
 import json
@@ -33,6 +40,12 @@ from workloads.metrics import nonfinite, rel_rmse
 
 FP16_INF_EDGE = 65520.0          # smallest magnitude that rounds to fp16 infinity
 STRICT_RANGE = 3.2e4             # |c * score| below which the strict variant is specified
+THETA = 4.0                      # the kernels' refine threshold on the tile maximum (log2 units)
+
+
+def block_keys(head_dim):
+    """Keys per block in the prefill kernels: 128 at head_dim 64, else 64."""
+    return 128 if head_dim == 64 else 64
 
 
 def points(full=False):
@@ -99,6 +112,56 @@ def _max_abs_scores(q, k, w, rows=None):
     return best
 
 
+def refine_rate(q, k, w, rows):
+    """Replay of PASA's per-block shift rule on the given flat row ids, in
+    binary64: per key block, mu = mean and m = max of the row's visible scaled
+    scores c*s (c = scale * log2 e); off = mu on the row's first visible block,
+    else max(mu, R); the block refines when fp16(m - off) exceeds THETA (or
+    overflows), and then off = m; R <- max(R, off + fp16(m - off)).  Returns
+    the refined fraction of (row, block) steps with a visible key."""
+    c = w.scale / math.log(2.0)
+    g = w.heads_q // w.heads_kv
+    bc = block_keys(w.head_dim)
+    h, i = np.divmod(rows, w.seqlen_q)
+    n_ref = n_tot = 0
+    for hh in np.unique(h):
+        ii = i[h == hh]
+        s = c * (q[0, ii, hh, :].astype(np.float64) @ k[0, :, hh // g, :].astype(np.float64).T)
+        lim = (ii + w.seqlen_kv - w.seqlen_q + 1) if w.causal else np.full(len(ii), w.seqlen_kv)
+        R = np.full(len(ii), -np.inf)
+        for b0 in range(0, w.seqlen_kv, bc):
+            blk = s[:, b0:b0 + bc]
+            vis = np.arange(b0, b0 + blk.shape[1])[None, :] < lim[:, None]
+            cnt = vis.sum(axis=1)
+            act = cnt > 0
+            mu = np.where(vis, blk, 0.0).sum(axis=1) / np.maximum(cnt, 1)
+            m = np.where(vis, blk, -np.inf).max(axis=1)
+            off = np.where(np.isinf(R), mu, np.maximum(mu, R))
+            with np.errstate(over="ignore", invalid="ignore"):
+                mb = (m - off).astype(np.float16).astype(np.float64)
+            ref = act & ~(mb <= THETA)
+            off = np.where(ref, m, off)
+            mb = np.where(ref, 0.0, mb)
+            R = np.where(act, np.maximum(R, off + mb), R)
+            n_ref += int(ref.sum())
+            n_tot += int(act.sum())
+    return n_ref / max(n_tot, 1)
+
+
+def replay(pt, seed=0, n_rows=256):
+    """The grid point's columns that need no GPU."""
+    w = workload(pt, seed)
+    q, k, _ = W.generate(w)
+    rng = np.random.default_rng(seed + 17)
+    rows = _rows(w, n_rows, rng)
+    all_rows = w.seqlen_q * w.seqlen_kv * w.heads_q <= (1 << 24)
+    mx = _max_abs_scores(q, k, w, None if all_rows else rows)
+    return dict(pt, heads=w.heads_q, max_abs_s=mx, s_rows="all" if all_rows else "sampled",
+                naive_overflow=bool(mx >= FP16_INF_EDGE),
+                max_abs_cs=mx * w.scale / math.log(2.0),
+                refine_rate=refine_rate(q, k, w, rows))
+
+
 def measure(pasa, pt, seed=0, n_rows=256):
     """Run one grid point through the three kernels and the oracle."""
     import torch
@@ -113,7 +176,8 @@ def measure(pasa, pt, seed=0, n_rows=256):
     h, i = np.divmod(rows, w.seqlen_q)
     res = dict(pt, heads=w.heads_q, max_abs_s=mx, s_rows="all" if all_rows else "sampled",
                naive_overflow=bool(mx >= FP16_INF_EDGE),
-               max_abs_cs=mx * w.scale / math.log(2.0))
+               max_abs_cs=mx * w.scale / math.log(2.0),
+               refine_rate=refine_rate(q, k, w, rows))
     for name, fn in (("naive", pasa.naive_attn_fwd), ("strict", pasa.attn_fwd_strict),
                      ("pasa", pasa.attn_fwd)):
         o, _ = fn(tq, tk, tv, causal=w.causal, scale=w.scale)
@@ -144,7 +208,13 @@ def onsets(results):
 def main():
     ap = argparse.ArgumentParser(description="designed-random sweep of the forward kernels")
     ap.add_argument("--full", action="store_true", help="the long grid (sequences to 65504)")
+    ap.add_argument("--replay-only", action="store_true",
+                    help="only the columns that need no GPU (scores, predicted overflow, refine rate)")
     args = ap.parse_args()
+    if args.replay_only:
+        for n, pt in enumerate(points(args.full)):
+            print(json.dumps(replay(pt, seed=100 + n)), flush=True)
+        return
     import precision_flashattention_numerics_amd as pasa
     results = []
     for n, pt in enumerate(points(args.full)):

@@ -301,20 +301,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __syncthreads();
     }
 
-    // ---- epilogue: global recovering
-    if (qi < Sq) {
+    // ---- epilogue: global recovering.  The K/V stages are free after the last
+    // barrier, so each wave stages its normalised fp16 rows in its own 32*D
+    // halves of LDS (16-byte chunks XOR-swizzled by row) and then writes whole
+    // rows: 16-byte stores, D/8 lanes per row, instead of scattered 8-byte ones.
+    {
+        constexpr int C = D / 8;   // 16-byte chunks per row
         const float L = row_sum<NAIVE>(st);
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        _Float16* orow = o + ((int64_t)b * Sq + qi) * q_stride + (int64_t)hq * D;
+        _Float16* const stg = smem + w * (32 * D);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const h4 t = {(_Float16)(acc[dt][4 * g + 0] * inv), (_Float16)(acc[dt][4 * g + 1] * inv),
                               (_Float16)(acc[dt][4 * g + 2] * inv), (_Float16)(acc[dt][4 * g + 3] * inv)};
-                *(h4*)(orow + 32 * dt + 8 * g + 4 * hh) = t;
+                const int ch = 4 * dt + g;   // columns 32*dt + 8*g .. +7; this lane's 4 at +4*hh
+                *(h4*)(stg + n * D + 8 * (ch ^ (n & (C - 1))) + 4 * hh) = t;
             }
-        if (lse != nullptr && hh == 0)
+#pragma unroll
+        for (int i = 0; i < C / 2; ++i) {
+            const int slot = 64 * i + lane;
+            const int row = slot / C, ch = slot % C;
+            const h8 val = *(const h8*)(stg + row * D + 8 * (ch ^ (row & (C - 1))));
+            if (wrow0 + row < Sq)
+                *(h8*)(o + ((int64_t)b * Sq + wrow0 + row) * q_stride + (int64_t)hq * D + 8 * ch) = val;
+        }
+        if (lse != nullptr && hh == 0 && qi < Sq)
             lse[((int64_t)b * Hq + hq) * Sq + qi] =
                 L > 0.0f ? (st.R + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
     }

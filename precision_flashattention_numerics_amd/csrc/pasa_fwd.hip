@@ -36,6 +36,8 @@
 //     one key/value head at a time, and causal tiles are issued longest first.
 //   * Blocks that every row of a wave sees in full take a branch-free path;
 //     only the diagonal / ragged-tail blocks evaluate the mask.
+//   * The epilogue stages each wave's normalised fp16 rows in the (by then
+//     free) LDS stages and writes whole rows with 16-byte stores.
 //
 // The per-block half-precision softmax (pseudo-average shift, refine, fp16
 // exponentials and sums) lives in pasa_tile.hpp.

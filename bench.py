@@ -65,15 +65,21 @@ PROFILE_CMDS = {
 
 
 def source_hash():
-    """sha256 over the kernel sources and the ABI header (what the counters describe)."""
+    """sha256 over the kernel sources and the ABI header (what the counters
+    describe), with comments and whitespace removed so that a comment edit
+    does not invalidate recorded counters."""
     import glob
     import hashlib
+    import re
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp")))
     files.append(os.path.join(ROOT, "include", "pasa_attn.h"))
     for f in files:
+        text = open(f).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
         h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -14,7 +14,8 @@
 //     K/V tiles in LDS and run in ping-pong: while one group issues its matrix
 //     products for a key block (P V of the previous block, then S^T = K Q^T of
 //     this one), the other group runs the half-precision softmax of its
-//     current block, and at every barrier they swap.  Each SIMD holds one wave
+//     current block, and at every phase boundary they swap (a barrier ends
+//     every odd phase, and at head_dim 64 every phase).  Each SIMD holds one wave
 //     of each group, so the matrix cores and the vector ALUs stay busy at the
 //     same time; the wave in its matrix phase runs at raised priority.
 //   * S^T = K Q^T on the matrix cores (v_mfma_f32_32x32x16_f16).  Q is the B

@@ -33,7 +33,7 @@ PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16 matrix peak
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E peak
 
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "prefill_c2_decode_c5_hbm_traffic.txt")
+TRAFFIC_FILE = os.path.join(PROFILES, "pasa_prefill_qwen2shape_s4096_decode_b64_kv8192_hbm_traffic.txt")
 CSRC = os.path.join(ROOT, "precision_flashattention_numerics_amd", "csrc")
 
 # Kernel symbols (substrings) of the profiled launches.
@@ -162,7 +162,7 @@ def summarize_profile(d):
             continue
         lines.append(f"{label:<28} {int(kv['Calls']):6d} {float(kv['AverageNs'])*1e-3:8.2f} "
                      f"{float(kv['MinNs'])*1e-3:8.2f} {float(kv['MaxNs'])*1e-3:8.2f}")
-    open(os.path.join(PROFILES, "prefill_c2_decode_c5_kernel_trace.txt"), "w").write("\n".join(lines) + "\n")
+    open(os.path.join(PROFILES, "pasa_prefill_qwen2shape_s4096_decode_b64_kv8192_kernel_trace.txt"), "w").write("\n".join(lines) + "\n")
 
     fetch = _counters(os.path.join(d, "fetch", "run_counter_collection.csv"))
     write = _counters(os.path.join(d, "write", "run_counter_collection.csv"))
@@ -206,7 +206,7 @@ def summarize_profile(d):
             vals = _pick(c, sub)
             rows.append(f"{name}: " + ", ".join(f"{k}={v:.0f}" for k, v in sorted(vals.items())))
     if rows:
-        open(os.path.join(PROFILES, "prefill_c2_decode_c5_counters.txt"), "w").write("\n".join(rows) + "\n")
+        open(os.path.join(PROFILES, "pasa_prefill_qwen2shape_s4096_decode_b64_kv8192_counters.txt"), "w").write("\n".join(rows) + "\n")
     print("\n".join(lines + t))
 
 

@@ -141,7 +141,7 @@ def summarize_profile(d):
              "kernel                         calls  avg_us    min_us    max_us   algorithmic    rate"]
     pre = st(K_PREFILL)
     avg_p = float(pre["AverageNs"]) * 1e-3
-    lines.append(f"pasa prefill (c2)            {int(pre['Calls']):6d} {avg_p:8.2f} "
+    lines.append(f"pasa prefill                 {int(pre['Calls']):6d} {avg_p:8.2f} "
                  f"{float(pre['MinNs'])*1e-3:8.2f} {float(pre['MaxNs'])*1e-3:8.2f}  "
                  f"{wp.flops():.4e} flop  {wp.flops()/avg_p/1e6:8.1f} TFLOP/s "
                  f"({wp.flops()/avg_p/1e6/PEAK_FP16_TFLOPS:.3f} of 2500)")
@@ -149,13 +149,13 @@ def summarize_profile(d):
     avg_s = float(sp["AverageNs"]) * 1e-3
     cb = st(K_COMBINE)
     avg_c = float(cb["AverageNs"]) * 1e-3
-    lines.append(f"pasa decode split (c5)       {int(sp['Calls']):6d} {avg_s:8.2f} "
+    lines.append(f"pasa decode split            {int(sp['Calls']):6d} {avg_s:8.2f} "
                  f"{float(sp['MinNs'])*1e-3:8.2f} {float(sp['MaxNs'])*1e-3:8.2f}  "
                  f"{wd.io_bytes():.4e} B     {wd.io_bytes()/avg_s/1e3:8.1f} GB/s "
                  f"({wd.io_bytes()/avg_s/1e3/PEAK_HBM_GBPS:.3f} of 8000)")
-    lines.append(f"pasa decode combine (c5)     {int(cb['Calls']):6d} {avg_c:8.2f} "
+    lines.append(f"pasa decode combine          {int(cb['Calls']):6d} {avg_c:8.2f} "
                  f"{float(cb['MinNs'])*1e-3:8.2f} {float(cb['MaxNs'])*1e-3:8.2f}")
-    for label, key in (("naive fp16 prefill (c2)", K_NAIVE), ("strict PASA prefill (c2)", K_STRICT)):
+    for label, key in (("naive fp16 prefill", K_NAIVE), ("strict PASA prefill", K_STRICT)):
         try:
             kv = st(key)
         except KeyError:
@@ -202,7 +202,7 @@ def summarize_profile(d):
             continue
         c = _counters(path)
         rows.append(f"# {title}: " + PROFILE_CMDS[key])
-        for name, sub in (("pasa prefill (c2)", K_PREFILL), ("pasa decode split (c5)", K_SPLIT)):
+        for name, sub in (("pasa prefill", K_PREFILL), ("pasa decode split", K_SPLIT)):
             vals = _pick(c, sub)
             rows.append(f"{name}: " + ", ".join(f"{k}={v:.0f}" for k, v in sorted(vals.items())))
     if rows:

@@ -149,10 +149,14 @@ int pasa_naive_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
  *               lse_part [batch, num_heads_q, n].  Its contents on return are
  *               the partials of this call.
  * Launches the split kernel and the combine kernel on `stream`, in order.
- * Errors: as pasa_attn_fwd (without the seqlen_kv bound), plus
- * PASA_ERR_WORKSPACE for a null, misaligned or too-small workspace, and
- * PASA_ERR_INVALID for num_splits < 0.  More splits than 32-key sub-tiles
- * are clamped to the number of sub-tiles.
+ * Errors: the argument checks of pasa_attn_fwd (without the seqlen_kv bound
+ * and the prefill work-item limit), plus PASA_ERR_WORKSPACE for a null,
+ * misaligned or too-small workspace, PASA_ERR_INVALID for num_splits < 0, and
+ * PASA_ERR_UNSUPPORTED when a split would sum more than 65504 keys, for more
+ * than 65535 splits, or when the split grid (batch * kv heads *
+ * ceil(gqa_group / 32) * splits waves) or the combine grid (batch *
+ * num_heads_q workgroups) exceeds 2^31 - 1.  More splits than 32-key
+ * sub-tiles are clamped to the number of sub-tiles.
  */
 int pasa_attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o,
                      float* lse, int batch, int seqlen_kv, int num_heads_q, int gqa_group,

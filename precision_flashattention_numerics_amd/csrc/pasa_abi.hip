@@ -37,9 +37,15 @@ int check_common(const void* q, const void* k, const void* v, const void* o, int
     // descriptor: 32-bit byte offsets
     if ((int64_t)seqlen_kv * (num_heads_q / gqa_group) * head_dim * 2 > 0xFFFFFFFFLL)
         return PASA_ERR_UNSUPPORTED;
-    if (seqlen_q > 65535 * 128) return PASA_ERR_UNSUPPORTED;   // grid y limit
-    if (batch > 65535) return PASA_ERR_UNSUPPORTED;            // grid z limit
     return PASA_OK;
+}
+
+// The decode launches one wave per (sequence, key/value head, chunk of 32
+// query heads, split) and one combine workgroup per (sequence, query head),
+// each a 1-D grid indexed by int.
+bool decode_grids_fit(int batch, int num_heads_q, int gqa_group, int n) {
+    const int64_t waves = (int64_t)batch * (num_heads_q / gqa_group) * ((gqa_group + 31) / 32) * n;
+    return waves <= 0x7FFFFFFFLL && (int64_t)batch * num_heads_q <= 0x7FFFFFFFLL;
 }
 
 int fwd_common(int variant, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -130,7 +136,7 @@ int pasa_attn_decode(const void* q, const void* k_cache, const void* v_cache, vo
                             : num_splits;
     const int blocks = (seqlen_kv + pasa::kDecodeBlock - 1) / pasa::kDecodeBlock;
     if (n > blocks) n = blocks;
-    if (n > 65535) return PASA_ERR_UNSUPPORTED;
+    if (n > 65535 || !decode_grids_fit(batch, num_heads_q, gqa_group, n)) return PASA_ERR_UNSUPPORTED;
     // every split sums at most 65504 keys in fp16
     const int per_split = (blocks + n - 1) / n * pasa::kDecodeBlock;
     if (per_split > kMaxFp16Sum) return PASA_ERR_UNSUPPORTED;
@@ -172,7 +178,7 @@ int pasa_attn_decode_paged(const void* q, const void* k_pages, const void* v_pag
                             : num_splits;
     const int blocks = (seqlen_kv + pasa::kDecodeBlock - 1) / pasa::kDecodeBlock;
     if (n > blocks) n = blocks;
-    if (n > 65535) return PASA_ERR_UNSUPPORTED;
+    if (n > 65535 || !decode_grids_fit(batch, num_heads_q, gqa_group, n)) return PASA_ERR_UNSUPPORTED;
     const int per_split = (blocks + n - 1) / n * pasa::kDecodeBlock;
     if (per_split > kMaxFp16Sum) return PASA_ERR_UNSUPPORTED;
     const size_t need = pasa_attn_decode_workspace_bytes(batch, num_heads_q, head_dim, n);

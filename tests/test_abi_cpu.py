@@ -90,6 +90,10 @@ def test_decode_validation_and_sizes(lib):
     assert dec(ws_ptr=None) == -3
     assert dec(ws_ptr=ctypes.c_void_p(0x1010)) == -3            # not 256-byte aligned
     assert dec(ws_bytes=ws - 1) == -3
+    # a combine grid (batch * num_heads_q workgroups) beyond 2^31 - 1
+    big = lib.pasa_attn_decode(P, P, P, P, None, 65535, 64, 65535, 65535, 64, ctypes.c_float(0.125),
+                               1, P, ctypes.c_size_t(1 << 62), None)
+    assert big == -2
 
 
 def test_combine_validation(lib):

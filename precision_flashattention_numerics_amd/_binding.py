@@ -87,6 +87,21 @@ def _want(t, name, dtype=torch.float16):
         raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor")
 
 
+def _want_shape(t, name, shape, dtype):
+    """A caller-supplied output buffer: the library writes through its pointer,
+    so dtype, device, layout and shape are checked here."""
+    _want(t, name, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _want_workspace(ws, device):
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    if ws.device != device:
+        raise ValueError("workspace must be on q's device")
+
+
 def _fwd(fn, where, q, k, v, causal, scale, out, lse, return_lse, stream):
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _want(t, nm)
@@ -197,10 +212,14 @@ def attn_decode(q, k_cache, v_cache, num_splits=0, scale=None, out=None, lse=Non
         scale = D ** -0.5
     if workspace is None:
         workspace, _ = decode_workspace(q, k_cache, num_splits)
+    _want_workspace(workspace, q.device)
     if out is None:
         out = torch.empty_like(q)
+    _want_shape(out, "out", q.shape, torch.float16)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _want_shape(lse, "lse", (B, Hq), torch.float32)
     rc = _lib.pasa_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B,
                                Skv, Hq, Hq // Hkv, D, float(scale), int(num_splits),
                                _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -235,10 +254,14 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, num_splits=0, 
         ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=q.device)
         off = (-ws.data_ptr()) % 256
         workspace = ws[off:off + nbytes]
+    _want_workspace(workspace, q.device)
     if out is None:
         out = torch.empty_like(q)
+    _want_shape(out, "out", q.shape, torch.float16)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _want_shape(lse, "lse", (B, Hq), torch.float32)
     rc = _lib.pasa_attn_decode_paged(
         _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(out),
         _ptr(lse), B, Hq, Hq // Hkv, D, page_size, num_pages, max_pages, float(scale),
@@ -257,8 +280,10 @@ def attn_decode_combine(o_part, lse_part, out=None, lse=None, stream=None):
         raise ValueError("lse_part must be [B,Hq,n]")
     if out is None:
         out = torch.empty((B, 1, Hq, D), dtype=torch.float16, device=o_part.device)
+    _want_shape(out, "out", (B, 1, Hq, D), torch.float16)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=o_part.device)
+    _want_shape(lse, "lse", (B, Hq), torch.float32)
     rc = _lib.pasa_attn_decode_combine(_ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse), B, Hq,
                                        D, n, _stream(stream))
     _check(rc, "pasa_attn_decode_combine")

@@ -264,6 +264,30 @@ def test_error_writes_nothing(pasa):
     assert bool((o == 7.0).all())
 
 
+def test_binding_rejects_wrong_output_buffers(pasa):
+    """The library writes through raw pointers, so the binding refuses output
+    buffers of the wrong shape, dtype or device before anything is launched."""
+    import torch
+    q = torch.zeros((2, 1, 4, 64), dtype=torch.float16, device="cuda")
+    k = torch.zeros((2, 64, 2, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        pasa.attn_decode(q, k, k, out=torch.empty((2, 1, 4, 32), dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError):
+        pasa.attn_decode(q, k, k, lse=torch.empty((2, 3), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        pasa.attn_decode(q, k, k, out=torch.empty_like(q, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        pasa.attn_decode(q, k, k, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    op = torch.zeros((2, 4, 3, 64), dtype=torch.float32, device="cuda")
+    lp = torch.zeros((2, 4, 3), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        pasa.attn_decode_combine(op, lp, out=torch.empty((2, 4, 64), dtype=torch.float16, device="cuda"))
+    qp = torch.zeros((1, 8, 2, 64), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        pasa.attn_fwd(qp, qp, qp, out=torch.empty((1, 8, 2, 32), dtype=torch.float16, device="cuda"))
+    torch.cuda.synchronize()
+
+
 # ----------------------------------------------------------------- limits
 @pytest.mark.parametrize("causal", [False, True])
 def test_max_kv_length_flat_rows(pasa, causal):

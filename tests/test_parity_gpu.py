@@ -326,3 +326,75 @@ def test_decode_deterministic_and_matches_prefill_shape(pasa):
     a, b = o1.cpu().numpy(), op.cpu().numpy()
     assert rel_rmse(a, b) <= 2 * REL_RMSE_MAX
     assert np.max(np.abs(l1.cpu().numpy() - lp.cpu().numpy()[:, :, 0])) <= 1e-2
+
+
+# ----------------------------------------------------------------- streams, graphs
+def test_concurrent_streams_match_serial(pasa):
+    """The library keeps no state: prefill and decode enqueued on two streams at
+    once give the results of running them one after the other."""
+    import torch
+    wp = W.custom(1, 300, 300, 7, 1, 128, True, kind="bias", seed=71, bias=20.0)
+    wd = W.custom(4, 1, 777, 8, 2, 64, False, kind="bias", seed=72, bias=20.0)
+    qp, kp, vp = to_gpu(*W.generate(wp))
+    qd, kd, vd = to_gpu(*W.generate(wd))
+    ref_p, ref_pl = pasa.attn_fwd(qp, kp, vp, causal=True, scale=wp.scale)
+    ws, n = pasa.decode_workspace(qd, kd)
+    ref_d, ref_dl = pasa.attn_decode(qd, kd, vd, scale=wd.scale, workspace=ws, num_splits=n)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    ws2, _ = pasa.decode_workspace(qd, kd, n)
+    outs = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            op, opl = pasa.attn_fwd(qp, kp, vp, causal=True, scale=wp.scale)
+        with torch.cuda.stream(s2):
+            od, odl = pasa.attn_decode(qd, kd, vd, scale=wd.scale, workspace=ws2, num_splits=n)
+        torch.cuda.synchronize()
+        outs.append((op, opl, od, odl))
+    for op, opl, od, odl in outs:
+        assert torch.equal(op, ref_p) and torch.equal(opl, ref_pl)
+        assert torch.equal(od, ref_d) and torch.equal(odl, ref_dl)
+
+
+def test_graph_replays_match_eager(pasa):
+    """Prefill and decode (split + combine) captured in a HIP graph: every
+    replay, with eager work and synchronisation between replays, reproduces the
+    eager results bit for bit (the path records no memset)."""
+    import torch
+    wp = W.custom(1, 257, 257, 4, 2, 64, True, kind="bias", seed=73, bias=25.0)
+    wd = W.custom(3, 1, 1000, 7, 1, 128, False, kind="bias", seed=74, bias=25.0)
+    qp, kp, vp = to_gpu(*W.generate(wp))
+    qd, kd, vd = to_gpu(*W.generate(wd))
+    ws, n = pasa.decode_workspace(qd, kd)
+    op = torch.empty_like(qp)
+    lp = torch.empty((1, 4, 257), dtype=torch.float32, device="cuda")
+    od = torch.empty_like(qd)
+    ld = torch.empty((3, 7), dtype=torch.float32, device="cuda")
+
+    def step():
+        pasa.attn_fwd(qp, kp, vp, causal=True, scale=wp.scale, out=op, lse=lp)
+        pasa.attn_decode(qd, kd, vd, scale=wd.scale, out=od, lse=ld, workspace=ws, num_splits=n)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (op, lp, od, ld)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):      # warm the capture stream, as torch recommends
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        for t in (op, lp, od, ld):
+            t.fill_(float("nan"))
+        junk = torch.randn(1 << 16, device="cuda").sum()   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say("replay", r, float(junk))
+        for t, rt in zip((op, lp, od, ld), ref):
+            assert torch.equal(t, rt), f"replay {r} differs"

@@ -95,7 +95,14 @@ __device__ __forceinline__ Item decode_item(int L, int N, int B, int Hq, int g, 
     return it;
 }
 
-template <int D, bool CAUSAL, int VAR>
+// KS (key split, non-causal only): a workgroup takes 128 query rows, and its two
+// ping-pong groups hold the same rows and take the two halves of the key range,
+// each staging its own K/V tiles; the epilogue merges the two partial results
+// (running maximum, running sum, accumulator) in fp32 with the same
+// log-sum-exp rule as the decode's combine.  Twice the work items of half the
+// length each: for problems whose 256-row items leave a partly idle last round
+// of workgroups (e.g. 360 items on 256 CUs).
+template <int D, bool CAUSAL, int VAR, bool KS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, _Float16* __restrict__ o, float* __restrict__ lse,
@@ -112,7 +119,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // takes the rest): at head_dim 64 the matrix phase has half the products
     // per score, so all of them go to the vector phase
     constexpr int EV = D == 64 ? 8 * NT : 0;
-    extern __shared__ __attribute__((aligned(1024))) _Float16 smem[];
+    static_assert(!(KS && CAUSAL), "the key split is for non-causal attention");
+    constexpr int kRows = KS ? kBR / 2 : kBR;   // query rows per workgroup
+    constexpr int kGroupStages = KS ? 2 : 1;    // stage sets: one per group with KS
+    __shared__ __attribute__((aligned(1024))) _Float16 smem[kGroupStages * fwd_smem_bytes<D>() / 2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -125,8 +135,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int hq = it.hq, b = it.b;
     const int Hkv = Hq / group;
     const int hkv = hq / group;
-    const int q0 = it.tile * kBR;
-    const int wrow0 = q0 + 32 * w;      // first query row of this wave
+    const int q0 = it.tile * kRows;
+    const int wr = KS ? (w & 3) : w;    // the wave's 32-row slot in the tile
+    const int wrow0 = q0 + 32 * wr;     // first query row of this wave
     const int qi = wrow0 + n;
 
     const int64_t q_stride = (int64_t)Hq * D;
@@ -141,10 +152,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int64_t shift = (int64_t)Skv - Sq;   // bottom-right causal alignment
     int kv_end = Skv;
     if (CAUSAL) {
-        const int64_t last = (int64_t)min(q0 + kBR - 1, Sq - 1) + shift;
+        const int64_t last = (int64_t)min(q0 + kRows - 1, Sq - 1) + shift;
         kv_end = last < 0 ? 0 : (int)min<int64_t>(Skv, last + 1);
     }
     const int nblocks = (kv_end + kBC - 1) / kBC;
+    // this wave's key blocks: [blk0, blk0 + nbl); with KS group 0 takes the
+    // first half (the longer one when odd) and group 1 the rest
+    const int nb0 = KS ? (nblocks + 1) / 2 : nblocks;
+    const int blk0 = KS ? __builtin_amdgcn_readfirstlane(grp ? nb0 : 0) : 0;   // wave-uniform
+    const int nbl = KS ? __builtin_amdgcn_readfirstlane(grp ? nblocks - nb0 : nb0) : nblocks;
     auto row_limit = [&](int row) -> int {   // keys [0, limit) are visible to row
         if (!CAUSAL) return Skv;
         const int64_t l = (int64_t)row + shift + 1;
@@ -153,27 +169,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int lim = row_limit(qi);
     const int wave_lim_lo = row_limit(wrow0);
     const int wave_lim_hi = row_limit(wrow0 + 31);
-    auto active = [&](int blk) { return blk < nblocks && blk * kBC < wave_lim_hi; };
+    // local block index j of this wave's range
+    auto active = [&](int j) { return j < nbl && (blk0 + j) * kBC < wave_lim_hi; };
 
-    _Float16* const Kst = smem;                           // 2 stages of K
-    _Float16* const Vst = smem + 2 * tile_halves<D>();    // 2 stages of V
-    // LDS DMA constants of this wave, and the stages' LDS byte addresses
-    const uint32_t w_u = __builtin_amdgcn_readfirstlane((uint32_t)w);
-    const TileDma<D, kBC, kWaves, false, FP8> kdma(FP8 ? (uint32_t)kv_stride : stride_b, w_u, lane);
-    const TileDma<D, kBC, kWaves, true> vdma(stride_b, w_u, lane);
+    // 2 stages of K then 2 of V (with KS: per group, the group's own)
+    const int sg = (KS && grp) ? 2 : 0;
+    _Float16* const Kst = smem + sg * tile_halves<D>();
+    _Float16* const Vst = smem + (2 * kGroupStages + sg) * tile_halves<D>();
+    // LDS DMA constants of this wave (the waves that share its tiles split the
+    // segments), and the stages' LDS byte addresses
+    constexpr int kLoadWaves = KS ? kWaves / 2 : kWaves;
+    const uint32_t w_u = __builtin_amdgcn_readfirstlane((uint32_t)(KS ? (w & 3) : w));
+    const TileDma<D, kBC, kLoadWaves, false, FP8> kdma(FP8 ? (uint32_t)kv_stride : stride_b, w_u, lane);
+    const TileDma<D, kBC, kLoadWaves, true> vdma(stride_b, w_u, lane);
     constexpr uint32_t kTileBytes = tile_halves<D>() * 2;
-    const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void*)smem;
+    const uint32_t k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)Kst);
+    const uint32_t v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)Vst);
     const uint32_t k_bytes = (uint32_t)(((int64_t)(Skv - 1) * kv_stride + D) * EB);
-    auto load_k = [&](int blk) {
-        const uint32_t off = (uint32_t)(blk * kBC) * (uint32_t)(kv_stride * EB);   // < k_bytes
-        kdma.issue(make_rsrc(kb + off, k_bytes - off), smem_lds + (blk & 1) * kTileBytes);
+    auto load_k = [&](int j) {   // local block j of this wave's range
+        const uint32_t off = (uint32_t)((blk0 + j) * kBC) * (uint32_t)(kv_stride * EB);   // < k_bytes
+        kdma.issue(make_rsrc(kb + off, k_bytes - off), k_lds + (j & 1) * kTileBytes);
     };
-    auto load_v = [&](int blk) {
-        const uint32_t off = (uint32_t)(blk * kBC) * stride_b;
+    auto load_v = [&](int j) {
+        const uint32_t off = (uint32_t)((blk0 + j) * kBC) * stride_b;
         vdma.issue(make_rsrc((const uint8_t*)vb + off, slab_bytes - off),
-                   smem_lds + (2 + (blk & 1)) * kTileBytes);
+                   v_lds + (j & 1) * kTileBytes);
     };
-    if (nblocks > 0) load_k(0);
+    if (nbl > 0) load_k(0);
 
     // ---- Q operand: lane holds Q[qi][16*kk + 8*hh .. +7]
     h8 qreg[FP8 ? 1 : KK];
@@ -262,7 +284,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // arguments; the accumulator rescale the new running maximum calls for
     auto vphase = [&](int j) {
         if (!active(j)) return;
-        const int kbase = j * kBC;
+        const int kbase = (blk0 + j) * kBC;
         _Float16 d;
         if (kbase + kBC <= wave_lim_lo) {   // the whole block is visible to the wave
             auto all = [](int, int) { return true; };
@@ -288,12 +310,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // Phase p: group 0 runs mphase(p/2) on even p and vphase(p/2) on odd p;
     // group 1 runs one phase behind.  K(m+1) and V(m) are loaded during phases
     // 2m and 2m+1 into the stages freed by K(m-1) and V(m-2).
-    const int nphase = nblocks > 0 ? 2 * nblocks + 2 : 0;
+    const int nphase = nb0 > 0 ? 2 * nb0 + 2 : 0;   // nb0: the longer of the ranges
     for (int p = 0; p < nphase; ++p) {
         if ((p & 1) == 0) {
             const int m = p >> 1;
-            if (m + 1 < nblocks) load_k(m + 1);
-            if (m < nblocks) load_v(m);
+            if (m + 1 < nbl) load_k(m + 1);
+            if (m < nbl) load_v(m);
         }
         const int pp = p - grp;   // this group's own phase index
         if (pp >= 0) {
@@ -314,15 +336,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
     }
 
-    // ---- epilogue: global recovering.  The K/V stages are free after the last
-    // barrier, so each wave stages its normalised fp16 rows in its own 32*D
-    // halves of LDS (16-byte chunks XOR-swizzled by row) and then writes whole
-    // rows: 16-byte stores, D/8 lanes per row, instead of scattered 8-byte ones.
+    // ---- epilogue: global recovering
+    constexpr int NV = DT * 16 + 2;                        // floats per lane handed over with KS
+    constexpr int kMergeHalves = KS ? 4 * NV * 64 * 2 : 0;  // LDS the hand-over takes (halves)
+    float Lf = row_sum<NAIVE>(st);   // running sum, relative to 2^Rf
+    float Rf = st.R;
+    if constexpr (KS) {
+        // merge the two key halves: group 1 hands its partial to its partner
+        // wave of group 0 through LDS (the stages are free after the last
+        // barrier), which rescales both to the larger maximum and adds them
+        float* const mb = (float*)smem + (w & 3) * (NV * 64);
+        if (grp == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mb[(16 * dt + r) * 64 + lane] = acc[dt][r];
+            mb[(NV - 2) * 64 + lane] = Rf;
+            mb[(NV - 1) * 64 + lane] = Lf;
+        }
+        __syncthreads();
+        if (grp == 1) return;
+        const float R1 = mb[(NV - 2) * 64 + lane];
+        const float L1 = mb[(NV - 1) * 64 + lane];
+        const float R = fmaxf(Rf, R1);
+        const bool any = R != -__builtin_inff();
+        const float a0 = any ? __builtin_amdgcn_exp2f(Rf - R) : 0.0f;   // 0 for a half with no key
+        const float a1 = any ? __builtin_amdgcn_exp2f(R1 - R) : 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[dt][r] = acc[dt][r] * a0 + mb[(16 * dt + r) * 64 + lane] * a1;
+        Lf = Lf * a0 + L1 * a1;
+        Rf = R;
+    }
+    // The K/V stages are free after the last barrier, so each wave stages its
+    // normalised fp16 rows in its own 32*D halves of LDS (16-byte chunks
+    // XOR-swizzled by row) and then writes whole rows: 16-byte stores, D/8
+    // lanes per row, instead of scattered 8-byte ones.
     {
         constexpr int C = D / 8;   // 16-byte chunks per row
-        const float L = row_sum<NAIVE>(st);
+        const float L = Lf;
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-        _Float16* const stg = smem + w * (32 * D);
+        _Float16* const stg = smem + kMergeHalves + wr * (32 * D);   // past the hand-over
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -342,33 +397,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
         if (lse != nullptr && hh == 0 && qi < Sq)
             lse[((int64_t)b * Hq + hq) * Sq + qi] =
-                L > 0.0f ? (st.R + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
+                L > 0.0f ? (Rf + __builtin_log2f(L)) * kLn2 : -__builtin_inff();
     }
 }
 
-template <int D, bool CAUSAL, int VAR>
+template <int D, bool CAUSAL, int VAR, bool KS>
 hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
-    auto kern = fwd_kernel<D, CAUSAL, VAR>;
-    constexpr int smem = fwd_smem_bytes<D>();
-    static_assert(smem <= 64 * 1024, "dynamic LDS above 64 KB would need an opt-in");
-    const int n_qtiles = (a.seqlen_q + kBR - 1) / kBR;
+    auto kern = fwd_kernel<D, CAUSAL, VAR, KS>;
+    static_assert((KS ? 2 : 1) * fwd_smem_bytes<D>() <= 160 * 1024, "LDS of one CU");
+    constexpr int rows = KS ? kBR / 2 : kBR;
+    const int n_qtiles = (a.seqlen_q + rows - 1) / rows;
     const int64_t n_items = (int64_t)a.batch * a.num_heads_q * n_qtiles;
-    hipLaunchKernelGGL(kern, dim3((unsigned)n_items), dim3(kThreads), smem, stream,
+    hipLaunchKernelGGL(kern, dim3((unsigned)n_items), dim3(kThreads), 0, stream,
                        (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
                        (_Float16*)a.o, a.lse, a.batch, a.seqlen_q, a.seqlen_kv, a.num_heads_q,
                        a.gqa_group, a.softmax_scale * a.qk_dequant * kLog2e, n_qtiles);
     return hipGetLastError();
 }
 
+// The key split pays when the 256-row items leave the last round of
+// workgroups partly idle: ceil(n128 / CUs) half-length rounds against
+// ceil(n256 / CUs) full ones (one workgroup per CU).
+bool use_key_split(const FwdArgs& a) {
+    if (a.causal) return false;
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n_cu < 1)
+        return false;
+    const int64_t heads = (int64_t)a.batch * a.num_heads_q;
+    const int64_t n256 = heads * ((a.seqlen_q + kBR - 1) / kBR);
+    const int64_t n128 = heads * ((a.seqlen_q + kBR / 2 - 1) / (kBR / 2));
+    if (n128 > 0x7FFFFFFFLL) return false;
+    return (n128 + n_cu - 1) / n_cu < 2 * ((n256 + n_cu - 1) / n_cu);
+}
+
+template <int D, int VAR>
+hipError_t launch_causal_or_not(const FwdArgs& a, hipStream_t stream) {
+    if (a.causal) return launch_one<D, true, VAR, false>(a, stream);
+    if (use_key_split(a)) return launch_one<D, false, VAR, true>(a, stream);
+    return launch_one<D, false, VAR, false>(a, stream);
+}
+
 template <int D>
 hipError_t launch_var(const FwdArgs& a, int variant, hipStream_t stream) {
-    if (variant == kVarNaive)
-        return a.causal ? launch_one<D, true, kVarNaive>(a, stream) : launch_one<D, false, kVarNaive>(a, stream);
-    if (variant == kVarStrict)
-        return a.causal ? launch_one<D, true, kVarStrict>(a, stream) : launch_one<D, false, kVarStrict>(a, stream);
-    if (variant == kVarFp8)
-        return a.causal ? launch_one<D, true, kVarFp8>(a, stream) : launch_one<D, false, kVarFp8>(a, stream);
-    return a.causal ? launch_one<D, true, kVarPasa>(a, stream) : launch_one<D, false, kVarPasa>(a, stream);
+    if (variant == kVarNaive) return launch_causal_or_not<D, kVarNaive>(a, stream);
+    if (variant == kVarStrict) return launch_causal_or_not<D, kVarStrict>(a, stream);
+    if (variant == kVarFp8) return launch_causal_or_not<D, kVarFp8>(a, stream);
+    return launch_causal_or_not<D, kVarPasa>(a, stream);
 }
 
 }  // namespace

@@ -328,6 +328,25 @@ def test_decode_deterministic_and_matches_prefill_shape(pasa):
     assert np.max(np.abs(l1.cpu().numpy() - lp.cpu().numpy()[:, :, 0])) <= 1e-2
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_noncausal_full_round_vs_oracle(pasa, D):
+    """A non-causal problem of exactly one round of 256-row items on 256 CUs
+    (64 heads x 1024 rows) keeps the 256-row kernel (the key split pays only for
+    a partly idle last round); small non-causal problems take the key split."""
+    w = W.custom(1, 1024, 1024, 64, 8, D, False, kind="bias", seed=75 + D, bias=25.0)
+    say("case", w)
+    (q, k, v), o, lse = run_fwd(pasa, w)
+    rng = np.random.default_rng(76)
+    rows = sample_rows(w, 3000, rng)
+    ro, rl = attn_fp64(q, k, v, w.scale, False, rows=rows)
+    go, gl = gather_rows(o, lse, w, rows)
+    assert nonfinite(o) == 0
+    err = rel_rmse(go, ro)
+    say("rel_rmse", err)
+    assert err <= REL_RMSE_MAX
+    assert lse_ok(gl, rl)
+
+
 # ----------------------------------------------------------------- streams, graphs
 def test_concurrent_streams_match_serial(pasa):
     """The library keeps no state: prefill and decode enqueued on two streams at

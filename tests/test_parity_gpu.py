@@ -391,13 +391,17 @@ def test_graph_replays_match_eager(pasa):
     od = torch.empty_like(qd)
     ld = torch.empty((3, 7), dtype=torch.float32, device="cuda")
 
+    on = torch.empty_like(qp)     # a non-causal prefill of few items takes the key split
+    ln = torch.empty_like(lp)
+
     def step():
         pasa.attn_fwd(qp, kp, vp, causal=True, scale=wp.scale, out=op, lse=lp)
+        pasa.attn_fwd(qp, kp, vp, causal=False, scale=wp.scale, out=on, lse=ln)
         pasa.attn_decode(qd, kd, vd, scale=wd.scale, out=od, lse=ld, workspace=ws, num_splits=n)
 
     step()
     torch.cuda.synchronize()
-    ref = [t.clone() for t in (op, lp, od, ld)]
+    ref = [t.clone() for t in (op, lp, on, ln, od, ld)]
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):      # warm the capture stream, as torch recommends
@@ -408,12 +412,12 @@ def test_graph_replays_match_eager(pasa):
     with torch.cuda.graph(g):
         step()
     for r in range(3):
-        for t in (op, lp, od, ld):
+        for t in (op, lp, on, ln, od, ld):
             t.fill_(float("nan"))
         junk = torch.randn(1 << 16, device="cuda").sum()   # eager work between replays
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         say("replay", r, float(junk))
-        for t, rt in zip((op, lp, od, ld), ref):
+        for t, rt in zip((op, lp, on, ln, od, ld), ref):
             assert torch.equal(t, rt), f"replay {r} differs"

@@ -492,6 +492,12 @@ def main():
         n_rows = int(min(total_rows, max(256, args.cpu_seconds * rate / (pairs(probe) / 256))))
         rows = np.sort(rng.choice(total_rows, n_rows, replace=False))
         ro, rl, tc = run_rows(rows)
+        # when the sample is the whole workload and takes less than the budget,
+        # repeat it until the budget is spent and take the median run
+        times = [tc]
+        while sum(times) < args.cpu_seconds and len(times) < 64:
+            times.append(run_rows(rows)[2])
+        tc = float(np.median(times))
         cpu_flops = 4 * wp.head_dim * pairs(rows)
         b, rem = np.divmod(rows, wp.heads_q * wp.seqlen_q)
         h, i = np.divmod(rem, wp.seqlen_q)
@@ -501,9 +507,11 @@ def main():
         out["strict_lse_max_abs_err_sampled"] = float(np.max(np.abs(ls_np[b, h, i] - rl)))
         cpu = {"value": cpu_flops / tc / 1e12, "unit": "TFLOP/s", "cores": num_threads(),
                "kind": "oracle",
-               "sample": f"{n_rows} random query rows of the prefill workload "
-                         f"({cpu_flops:.3e} algorithmic flops, {tc:.1f} s, binary64, OpenMP)"}
-        log(f"oracle: {n_rows} rows in {tc:.1f} s")
+               "sample": (f"{'all ' if n_rows == total_rows else ''}{n_rows} "
+                          f"{'' if n_rows == total_rows else 'random '}query rows of the prefill "
+                          f"workload ({cpu_flops:.3e} algorithmic flops, binary64, OpenMP), "
+                          f"median of {len(times)} runs over {sum(times):.1f} s: {tc:.2f} s per run")}
+        log(f"oracle: {n_rows} rows, {len(times)} runs, median {tc:.2f} s")
 
     line = {
         "metric": "PASA fwd TFLOP/s (fraction of fp16 MFMA peak); decode HBM GB/s; RMSE vs fp64",

@@ -109,7 +109,9 @@ int pasa_attn_decode_splits(int batch, int seqlen_kv, int num_heads_q, int gqa_g
         num_heads_q % gqa_group != 0)
         return 0;
     const int64_t units = (int64_t)batch * (num_heads_q / gqa_group) * ((gqa_group + 31) / 32);
-    const int64_t target = 768;    // waves: three per compute unit on 256 CUs (LDS-limited)
+    // waves: two per compute unit on 256 CUs.  LDS would hold three, but fewer
+    // and longer key streams per sequence read the cache faster.
+    const int64_t target = 512;
     int64_t n = (target + units - 1) / units;
     const int64_t blocks = (seqlen_kv + pasa::kDecodeBlock - 1) / pasa::kDecodeBlock;
     if (n > blocks) n = blocks;

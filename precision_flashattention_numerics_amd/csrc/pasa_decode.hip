@@ -96,14 +96,28 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     const int kend = min(kbeg + split_len, Skv);
     const int nsub = (kend - kbeg + kSub - 1) / kSub;
 
+    // Paged: the split's page indices, 64 at a time, one per lane (lane l holds
+    // entry pbase + 64 * pchunk + l of the sequence's block table; -1 past its
+    // end), so that a sub-tile's page is a lane read, not a dependent memory
+    // load in front of every DMA.
+    const int pbase = PAGED ? kbeg / pg.page_size : 0;
+    int pchunk = 0, pcache = -1;
+    auto load_pages = [&](int ch) {
+        const int idx = pbase + 64 * ch + lane;
+        pcache = idx < pg.max_pages ? pg.block_table[(int64_t)b * pg.max_pages + idx] : -1;
+        pchunk = ch;
+    };
+    if (PAGED) load_pages(0);
+
     auto slot_k = [&](int j) { return smem + (j % kSlots) * 2 * sub_halves<D>(); };
     auto issue = [&](int j) {
         _Float16* sk = slot_k(j);
         const int key0 = kbeg + j * kSub;
         if (PAGED) {
             // the sub-tile's page, and a descriptor over its rows that exist
-            const int page = __builtin_amdgcn_readfirstlane(
-                pg.block_table[(int64_t)b * pg.max_pages + key0 / pg.page_size]);
+            const int pl = __builtin_amdgcn_readfirstlane(key0 / pg.page_size - pbase);
+            if (__builtin_amdgcn_readfirstlane(pl >> 6) != pchunk) load_pages(pl >> 6);   // rare
+            const int page = __builtin_amdgcn_readlane(pcache, pl & 63);
             const int rows = min(kSub, Skv - key0);
             const bool ok = page >= 0 && page < pg.num_pages;
             const int64_t base = ((int64_t)(ok ? page : 0) * pg.page_size + key0 % pg.page_size) *

@@ -9,19 +9,22 @@
 //
 //   mu    = mean of the row's visible scores S in the block         (fp32)
 //   off   = c*mu on the row's first visible block, else max(c*mu, R) (fp32)
-//   T     = fp16_rne(c*S - off) (one rounding), masked keys -> -inf   (fp16)
-//   m_b   = max_j T                                                   (fp16)
+//   m_b   = fp16_rne(c*max_j S - off), the largest entry of the
+//           shifted fp16 tile                                          (fp16)
 //   if m_b > THETA (the tile's largest entries would sit where fp16 is
-//   coarse, or overflow): off = max_j c*S over visible keys, and T, m_b
-//   are taken relative to that instead
+//   coarse, or overflow): off = max_j c*S over visible keys, and m_b is
+//   taken relative to that instead
 //   R'    = max(R, off + m_b)      running maximum, log2 units        (fp32)
-//   s     = fp16(R' - off);  P = exp2(T - s);  r = sum_j P            (fp16)
+//   s     = fp16(R' - off)                                            (fp16)
+//   X     = fp16_rne(c*S - (off + s)) (one rounding), masked keys -> -inf
+//   P     = exp2(X);  r = sum_j P                                     (fp16)
 //   alpha = exp2(fp16(R - R'))                                        (fp16)
 //   (l_hi, l_lo) <- compensated fp16 sum of alpha*(l_hi, l_lo) + r    (fp16)
-// where c = scale * log2(e).  Because T and s are taken relative to the same
-// off, P = exp2(c*S - R') whatever off was: the shift changes only which fp16
-// numbers are formed, never the softmax (a per-row shift leaves softmax
-// unchanged).  The epilogue recovers the exact log-sum-exp as
+// where c = scale * log2(e).  X is the shifted tile fp16(c*S - off) moved
+// down by s, formed in a single rounding (s is known before the tile is
+// formed).  Because X is taken against off + s, P = exp2(c*S - R') up to
+// rounding whatever off was: the shift changes only which fp16 numbers are
+// formed, never the softmax (a per-row shift leaves softmax unchanged).  The epilogue recovers the exact log-sum-exp as
 // ln2 * (R + log2(l_hi + l_lo)).
 //
 // The naive variant rounds the UNSCALED S to fp16, scales it in fp16 and
@@ -71,8 +74,8 @@ struct RowState {
 // One key block of NT 32-key sub-tiles for the row held by this lane (and by
 // the lane 32 apart, which holds the other half of the row's keys), in two
 // steps that a kernel may run at different times:
-//   softmax_tile  the shift, the fp16 tile T and the exponent arguments
-//                 X = T - s; updates the running maximum and returns
+//   softmax_tile  the shift and the fp16 exponent arguments X (the
+//                 shifted tile less s); updates the running maximum and returns
 //                 d = fp16(R - R') (0 when the row sees no key of the block)
 //   softmax_exp   P = exp2(X) in place, the row sum r, and the running sum
 //                 rescaled by alpha = exp2(d), the factor the caller also
@@ -88,8 +91,9 @@ struct RowState {
 // The tile maximum m_b = max_j fp16(c*S_j - off) equals fp16(c*max_j S_j - off)
 // because rounding to fp16 is monotone; it is therefore taken from one fp32
 // max pass that runs beside the pseudo-average sum, and the refine decision
-// (m_b > THETA -> centre at the row maximum) is made before the fp16 tile is
-// formed, so the tile is formed exactly once and without a branch.
+// (m_b > THETA -> centre at the row maximum) is made before any fp16 entry is
+// formed, so the exponent arguments are formed exactly once and without a
+// branch.
 //
 // STRICT (PASA only) also holds the running maximum R and the offset off in
 // fp16: each is rounded to fp16 where it is formed, and R' = max(R, off + m_b)
@@ -150,7 +154,13 @@ __device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 
             off = r16(c * m32);
             mb = fma_to_h(m32, c, -off);
         }
-        const float noff = -off;
+        // the running maximum and s are known at this point, so the exponent
+        // argument (the shifted tile less s) is formed in one rounding:
+        // X = fp16(c*S - (off + s))
+        const float top = STRICT ? (float)((_Float16)off + mb) : off + (float)mb;
+        const float Rn = cnt > 0 ? fmaxf(st.R, top) : st.R;
+        const _Float16 s = cnt > 0 ? (_Float16)(Rn - off) : (_Float16)0;
+        const float noff = -(off + (float)s);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -162,6 +172,9 @@ __device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 
                 }
                 X[8 * t + r / 2] = x;
             }
+        const _Float16 d = cnt > 0 ? (_Float16)(st.R - Rn) : (_Float16)0;
+        st.R = Rn;
+        return d;
     } else {
         const _Float16 ch = (_Float16)c;
         h2 mm = (h2){kHalfNegInf, kHalfNegInf};

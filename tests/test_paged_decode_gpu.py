@@ -134,3 +134,41 @@ def test_paged_out_of_range_page_reads_zero(pasa):
     assert nonfinite(o) == 0
     assert rel_rmse(o, ro) <= REL_RMSE_MAX
     assert lse_ok(lse, rl)
+
+
+@pytest.mark.parametrize("S,ps,splits", [(8192, 32, 1), (8192, 32, 3), (16384, 64, 3)])
+def test_paged_long_splits_match_contiguous_bitwise(pasa, S, ps, splits):
+    """Splits that span more than 64 pages: the page indices of a split are
+    taken from the block table 64 at a time, so these cross one or more such
+    boundaries (and at page_size 64 with 3 splits the second split starts in
+    the middle of a page)."""
+    import torch
+    B, Hq, Hkv, D = 2, 8, 2, 128
+    say("paged long split", S, ps, splits)
+    w = W.custom(B, 1, S, Hq, Hkv, D, False, kind="bias", seed=91, bias=30.0)
+    q, k, v = W.generate(w)
+    tq, tk, tv = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    oc, lc = pasa.attn_decode(tq, tk, tv, num_splits=splits, scale=w.scale)
+    kpool = tk.reshape(B * S // ps, ps, Hkv, D)
+    vpool = tv.reshape(B * S // ps, ps, Hkv, D)
+    table = torch.arange(B * S // ps, dtype=torch.int32, device="cuda").reshape(B, S // ps)
+    lens = torch.full((B,), S, dtype=torch.int32, device="cuda")
+    op, lp = pasa.attn_decode_paged(tq, kpool, vpool, table, lens, num_splits=splits,
+                                    scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(oc, op)
+    assert torch.equal(lc, lp)
+
+
+def test_paged_single_split_over_shuffled_pool_vs_oracle(pasa):
+    """One split over 256 shuffled 32-key pages (four groups of 64 table
+    entries), against the oracle on the gathered keys."""
+    lens, Hq, Hkv, D, ps = [8192, 5000], 8, 2, 128, 32
+    q, kp, vp, table, ln = paged_case(len(lens), lens, Hq, Hkv, D, ps, seed=13)
+    o, lse, scale = run_paged(pasa, q, kp, vp, table, ln, num_splits=1)
+    ro, rl = oracle_paged(q, kp, vp, table, ln, scale)
+    assert nonfinite(o) == 0
+    err = rel_rmse(o, ro)
+    say("rel_rmse", err)
+    assert err <= REL_RMSE_MAX
+    assert lse_ok(lse, rl)

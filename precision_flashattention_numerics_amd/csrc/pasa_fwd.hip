@@ -236,12 +236,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // and row sums of block j-1 issued between the products, then P V for
     // block j-1, as one straight-line region whose LDS operand reads are kept
     // several products ahead of their use
-    auto mphase = [&](int j) {
+    auto mphase_at = [&](int j, const _Float16* Ks, const _Float16* Vs) __attribute__((always_inline)) {
         __builtin_amdgcn_s_setprio(1);
         const bool pv = j >= 1 && active(j - 1);
         const bool qk = active(j);
-        const _Float16* Vs = Vst + ((j - 1) & 1) * tile_halves<D>();
-        const _Float16* Ks = Kst + (j & 1) * tile_halves<D>();
         if (pv && qk) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) S[t] = qk_sub(Ks, 32 * t);
@@ -279,6 +277,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         }
         __builtin_amdgcn_s_setprio(0);
+    };
+    // one copy of the matrix phase per stage parity, so that the stages' LDS
+    // addresses are constants of each copy
+    auto mphase = [&](int j) {
+        if (j & 1) mphase_at(j, Kst + tile_halves<D>(), Vst);
+        else mphase_at(j, Kst, Vst + tile_halves<D>());
     };
     // vector phase of block j: the shift, the fp16 tile and its exponent
     // arguments; the accumulator rescale the new running maximum calls for

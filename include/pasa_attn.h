@@ -195,10 +195,13 @@ int pasa_attn_decode_paged(const void* q, const void* k_pages, const void* v_pag
                            int num_splits, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
-/* The split count pasa_attn_decode uses for num_splits = 0 (host function, no
- * device work): enough (sequence, key/value head, split) work items to fill the
- * chip, clamped to the number of 32-key sub-tiles.  Returns 0 on invalid sizes. */
-int pasa_attn_decode_splits(int batch, int seqlen_kv, int num_heads_q, int gqa_group);
+/* The split count pasa_attn_decode and pasa_attn_decode_paged use for
+ * num_splits = 0 (host function, no device work): enough (sequence, key/value
+ * head, split) work items for two waves per compute unit at head_dim 128 and
+ * three at head_dim 64, clamped to the number of 32-key sub-tiles.  Returns 0
+ * on invalid sizes, including a head_dim other than 64 or 128. */
+int pasa_attn_decode_splits(int batch, int seqlen_kv, int num_heads_q, int gqa_group,
+                            int head_dim);
 
 /* Workspace size in bytes for pasa_attn_decode with num_splits splits (host
  * function).  Returns 0 on invalid sizes. */

@@ -39,7 +39,7 @@ _lib.pasa_attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _
                                         _i, _f, _i, _vp, _sz, _vp]
 _lib.pasa_attn_decode_paged.restype = _i
 _lib.pasa_attn_decode.restype = _i
-_lib.pasa_attn_decode_splits.argtypes = [_i, _i, _i, _i]
+_lib.pasa_attn_decode_splits.argtypes = [_i, _i, _i, _i, _i]
 _lib.pasa_attn_decode_splits.restype = _i
 _lib.pasa_attn_decode_workspace_bytes.argtypes = [_i, _i, _i, _i]
 _lib.pasa_attn_decode_workspace_bytes.restype = _sz
@@ -178,8 +178,8 @@ def naive_attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, return
                 lse, return_lse, stream)
 
 
-def decode_splits(batch, seqlen_kv, num_heads_q, gqa_group) -> int:
-    return int(_lib.pasa_attn_decode_splits(batch, seqlen_kv, num_heads_q, gqa_group))
+def decode_splits(batch, seqlen_kv, num_heads_q, gqa_group, head_dim) -> int:
+    return int(_lib.pasa_attn_decode_splits(batch, seqlen_kv, num_heads_q, gqa_group, head_dim))
 
 
 def decode_workspace_bytes(batch, num_heads_q, head_dim, num_splits) -> int:
@@ -190,7 +190,7 @@ def decode_workspace(q, k_cache, num_splits=0):
     """Allocate a workspace (uint8 tensor, 256-byte aligned) for attn_decode."""
     B, _, Hq, D = q.shape
     _, Skv, Hkv, _ = k_cache.shape
-    n = num_splits or decode_splits(B, Skv, Hq, Hq // Hkv)
+    n = num_splits or decode_splits(B, Skv, Hq, Hq // Hkv, D)
     nbytes = decode_workspace_bytes(B, Hq, D, n)   # the library may use fewer splits
     ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=q.device)
     off = (-ws.data_ptr()) % 256
@@ -249,7 +249,7 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, num_splits=0, 
     if scale is None:
         scale = D ** -0.5
     if workspace is None:
-        n = num_splits or decode_splits(B, page_size * max_pages, Hq, Hq // Hkv)
+        n = num_splits or decode_splits(B, page_size * max_pages, Hq, Hq // Hkv, D)
         nbytes = decode_workspace_bytes(B, Hq, D, n)
         ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=q.device)
         off = (-ws.data_ptr()) % 256

@@ -104,14 +104,16 @@ int pasa_naive_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
                       gqa_group, head_dim, softmax_scale, causal, stream);
 }
 
-int pasa_attn_decode_splits(int batch, int seqlen_kv, int num_heads_q, int gqa_group) {
+int pasa_attn_decode_splits(int batch, int seqlen_kv, int num_heads_q, int gqa_group,
+                            int head_dim) {
     if (batch < 1 || seqlen_kv < 1 || num_heads_q < 1 || gqa_group < 1 ||
-        num_heads_q % gqa_group != 0)
+        num_heads_q % gqa_group != 0 || (head_dim != 64 && head_dim != 128))
         return 0;
     const int64_t units = (int64_t)batch * (num_heads_q / gqa_group) * ((gqa_group + 31) / 32);
-    // waves: two per compute unit on 256 CUs.  LDS would hold three, but fewer
-    // and longer key streams per sequence read the cache faster.
-    const int64_t target = 512;
+    // waves on 256 CUs, measured: at head_dim 128 two per CU (LDS would hold
+    // three, but fewer and longer key streams per sequence read the cache
+    // faster); at head_dim 64 three per CU (of the six LDS holds)
+    const int64_t target = head_dim == 64 ? 768 : 512;
     int64_t n = (target + units - 1) / units;
     const int64_t blocks = (seqlen_kv + pasa::kDecodeBlock - 1) / pasa::kDecodeBlock;
     if (n > blocks) n = blocks;
@@ -134,7 +136,7 @@ int pasa_attn_decode(const void* q, const void* k_cache, const void* v_cache, vo
                           head_dim, softmax_scale);
     if (rc != PASA_OK) return rc;
     if (num_splits < 0) return PASA_ERR_INVALID;
-    int n = num_splits == 0 ? pasa_attn_decode_splits(batch, seqlen_kv, num_heads_q, gqa_group)
+    int n = num_splits == 0 ? pasa_attn_decode_splits(batch, seqlen_kv, num_heads_q, gqa_group, head_dim)
                             : num_splits;
     const int blocks = (seqlen_kv + pasa::kDecodeBlock - 1) / pasa::kDecodeBlock;
     if (n > blocks) n = blocks;
@@ -176,7 +178,7 @@ int pasa_attn_decode_paged(const void* q, const void* k_pages, const void* v_pag
     if (!fits(num_pages, page_size, num_heads_q / gqa_group, head_dim)) return PASA_ERR_UNSUPPORTED;
     if ((int64_t)batch * max_pages_per_seq > 0x7fffffff) return PASA_ERR_UNSUPPORTED;
     if (num_splits < 0) return PASA_ERR_INVALID;
-    int n = num_splits == 0 ? pasa_attn_decode_splits(batch, seqlen_kv, num_heads_q, gqa_group)
+    int n = num_splits == 0 ? pasa_attn_decode_splits(batch, seqlen_kv, num_heads_q, gqa_group, head_dim)
                             : num_splits;
     const int blocks = (seqlen_kv + pasa::kDecodeBlock - 1) / pasa::kDecodeBlock;
     if (n > blocks) n = blocks;

@@ -75,10 +75,12 @@ def test_decode_validation_and_sizes(lib):
     rows = 64 * 28 * 4
     assert ws == ((rows * 128 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
     assert lib.pasa_attn_decode_workspace_bytes(0, 28, 128, 4) == 0
-    assert lib.pasa_attn_decode_splits(64, 8192, 28, 7) >= 1
-    assert lib.pasa_attn_decode_splits(1, 100, 1, 1) == 4      # four 32-key sub-tiles
-    assert lib.pasa_attn_decode_splits(1, 20, 1, 1) == 1
-    assert lib.pasa_attn_decode_splits(1, 8192, 28, 3) == 0    # 28 % 3 != 0
+    assert lib.pasa_attn_decode_splits(64, 8192, 28, 7, 128) == 2   # 512 waves over 256 units
+    assert lib.pasa_attn_decode_splits(64, 8192, 28, 7, 64) == 3    # 768 waves
+    assert lib.pasa_attn_decode_splits(1, 100, 1, 1, 128) == 4      # four 32-key sub-tiles
+    assert lib.pasa_attn_decode_splits(1, 20, 1, 1, 64) == 1
+    assert lib.pasa_attn_decode_splits(1, 8192, 28, 3, 128) == 0    # 28 % 3 != 0
+    assert lib.pasa_attn_decode_splits(1, 8192, 28, 7, 96) == 0     # unsupported head_dim
 
     def dec(ws_ptr=P, ws_bytes=1 << 30, D=128, n=4, g=7, q=P):
         return lib.pasa_attn_decode(q, P, P, P, None, 64, 8192, 28, g, D, ctypes.c_float(0.08),

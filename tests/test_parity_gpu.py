@@ -203,7 +203,8 @@ def test_c5_decode_vs_oracle(pasa):
 
 @pytest.mark.parametrize("Skv,n,Hq,Hkv,D", [(1, 0, 4, 1, 128), (129, 3, 7, 7, 64),
                                             (1000, 0, 28, 4, 128), (5000, 7, 40, 1, 64),
-                                            (8192, 1, 8, 8, 128), (300, 64, 14, 2, 128)])
+                                            (8192, 1, 8, 8, 128), (300, 64, 14, 2, 128),
+                                            (2000, 0, 16, 2, 64)])
 def test_decode_shapes_vs_oracle(pasa, Skv, n, Hq, Hkv, D):
     import torch
     w = W.custom(3, 1, Skv, Hq, Hkv, D, False, kind="bias", seed=Skv + n, bias=30.0)

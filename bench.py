@@ -44,22 +44,22 @@ K_SPLIT = "decode_split_kernelILi128ELb0E"   # decode split, head_dim 128, conti
 K_COMBINE = "decode_combine_kernel"
 
 PROFILE_CMDS = {
-    "trace": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/trace -o run --output-format csv "
+    "trace": "rocprofv3 --kernel-trace --stats -d rocprof_out/trace -o run --output-format csv "
              "-- python bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-other-configs",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/fetch -o run --output-format csv "
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -d rocprof_out/fetch -o run --output-format csv "
              "-- python bench.py --steps 3 --warmup 1 --warm-seconds 0 --no-cpu-baseline --no-other-configs",
-    "write": "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/write -o run --output-format csv "
+    "write": "rocprofv3 --pmc WRITE_SIZE -d rocprof_out/write -o run --output-format csv "
              "-- python bench.py --steps 3 --warmup 1 --warm-seconds 0 --no-cpu-baseline --no-other-configs",
-    "cfetch": "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof/cfetch -o run --output-format csv "
+    "cfetch": "rocprofv3 --pmc FETCH_SIZE -d rocprof_out/cfetch -o run --output-format csv "
               "-- python bench.py --calibrate-copy 1024",
-    "cwrite": "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof/cwrite -o run --output-format csv "
+    "cwrite": "rocprofv3 --pmc WRITE_SIZE -d rocprof_out/cwrite -o run --output-format csv "
               "-- python bench.py --calibrate-copy 1024",
     "pmc1": "rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU "
-            "SQ_INSTS_VMEM SQ_BUSY_CYCLES SQ_WAVE_CYCLES -d gpurun_out/prof/pmc1 -o run "
+            "SQ_INSTS_VMEM SQ_BUSY_CYCLES SQ_WAVE_CYCLES -d rocprof_out/pmc1 -o run "
             "--output-format csv -- python bench.py --steps 3 --warmup 1 --warm-seconds 0 --no-cpu-baseline --no-other-configs",
     "pmc2": "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU "
             "SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_ACTIVE_INST_ANY SQ_WAIT_ANY GRBM_GUI_ACTIVE "
-            "-d gpurun_out/prof/pmc2 -o run --output-format csv -- python bench.py --steps 3 "
+            "-d rocprof_out/pmc2 -o run --output-format csv -- python bench.py --steps 3 "
             "--warmup 1 --warm-seconds 0 --no-cpu-baseline --no-other-configs",
 }
 

@@ -7,17 +7,24 @@ One step = the whole hot path over one batch of synthetic input:
     token, 28/4 heads, head_dim 128, KV length 8192).
 `value` is the prefill's TFLOP/s over algorithmic flops (4 * head_dim per
 visible query/key pair), from HIP events recorded on the launch stream around
-each prefill call inside the timed steps; the decode's achieved HBM GB/s is
-reported beside it.  Inputs are resident in HBM before timing starts, and
-the timed steps follow --warm-seconds of back-to-back warmup steps: the GPU
-raises its clock only after tens of milliseconds of sustained load, so a
-burst timed right after an idle spell measures the clock ramp instead of the
-kernel (that cold figure is reported beside it as prefill_ms_cold).
+the prefill launches inside the timed steps; the decode's achieved HBM GB/s is
+reported beside it.  Inputs are resident in HBM before timing starts, and the
+timed steps follow back-to-back warmup steps -- at least --warmup of them and
+at least --warm-seconds of wall time, both counted in the line: the GPU raises
+its clock only after tens of milliseconds of sustained load, so a burst timed
+right after an idle spell measures the clock ramp instead of the kernel (that
+cold figure is reported beside it as prefill_ms_cold).
 
-Also reported: relative RMSE of sampled output rows against the binary64
-oracle, the naive fp16 kernel's inf/NaN count on the same input (the overflow
-PASA avoids), and the oracle itself timed on this host's cores over a bounded
-row sample (`cpu_baseline`).
+Also reported: the roofline fractions against the published peaks and against
+peaks measured on this GPU by two microbenchmarks (back-to-back fp16 matrix
+products; a streaming HBM read); the other prefill workloads (single head,
+Stable-Video-Diffusion-shaped resonance, 32K long context) with the naive fp16
+kernel's overflow on each; relative RMSE of sampled output rows against the
+binary64 oracle; and the oracle itself timed on this host's cores over a
+bounded row sample (`cpu_baseline`).
+
+`--profile-config c3|c4` runs only that prefill workload (for rocprofv3), and
+`--summarize-profile DIR SET` writes the text summaries under profiles/.
 """
 import argparse
 import json
@@ -29,39 +36,65 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16 matrix peak
-PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E peak
+PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16 matrix peak (published)
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E peak (published)
 
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "pasa_prefill_qwen2shape_s4096_decode_b64_kv8192_hbm_traffic.txt")
 CSRC = os.path.join(ROOT, "precision_flashattention_numerics_amd", "csrc")
+PEAK_LIB = os.path.join(ROOT, "precision_flashattention_numerics_amd", "peak", "libpasa_peak.so")
 
-# Kernel symbols (substrings) of the profiled launches.
-K_PREFILL = "fwd_kernelILi128ELb1ELi0E"      # PASA prefill, head_dim 128, causal
-K_STRICT = "fwd_kernelILi128ELb1ELi1E"       # strict PASA prefill, same shape
-K_NAIVE = "fwd_kernelILi128ELb1ELi2E"        # naive fp16 prefill, same shape
+# Kernel symbols (substrings) of the profiled launches:
+# fwd_kernel<head_dim, causal, variant (0 PASA, 1 strict, 2 naive, 3 e4m3), key split>
+K_PREFILL = "fwd_kernelILi128ELb1ELi0ELb0E"  # PASA prefill, head_dim 128, causal
+K_STRICT = "fwd_kernelILi128ELb1ELi1ELb0E"   # strict PASA prefill, same shape
+K_NAIVE = "fwd_kernelILi128ELb1ELi2ELb0E"    # naive fp16 prefill, same shape
+K_C3 = "fwd_kernelILi64ELb0ELi0ELb1E"        # PASA prefill, head_dim 64, non-causal, key split
 K_SPLIT = "decode_split_kernelILi128ELb0E"   # decode split, head_dim 128, contiguous cache
 K_COMBINE = "decode_combine_kernel"
 
-PROFILE_CMDS = {
-    "trace": "rocprofv3 --kernel-trace --stats -d rocprof_out/trace -o run --output-format csv "
-             "-- python bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-other-configs",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE -d rocprof_out/fetch -o run --output-format csv "
-             "-- python bench.py --steps 3 --warmup 1 --warm-seconds 0 --no-cpu-baseline --no-other-configs",
-    "write": "rocprofv3 --pmc WRITE_SIZE -d rocprof_out/write -o run --output-format csv "
-             "-- python bench.py --steps 3 --warmup 1 --warm-seconds 0 --no-cpu-baseline --no-other-configs",
-    "cfetch": "rocprofv3 --pmc FETCH_SIZE -d rocprof_out/cfetch -o run --output-format csv "
-              "-- python bench.py --calibrate-copy 1024",
-    "cwrite": "rocprofv3 --pmc WRITE_SIZE -d rocprof_out/cwrite -o run --output-format csv "
-              "-- python bench.py --calibrate-copy 1024",
-    "pmc1": "rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU "
-            "SQ_INSTS_VMEM SQ_BUSY_CYCLES SQ_WAVE_CYCLES -d rocprof_out/pmc1 -o run "
-            "--output-format csv -- python bench.py --steps 3 --warmup 1 --warm-seconds 0 --no-cpu-baseline --no-other-configs",
-    "pmc2": "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU "
-            "SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_ACTIVE_INST_ANY SQ_WAIT_ANY GRBM_GUI_ACTIVE "
-            "-d rocprof_out/pmc2 -o run --output-format csv -- python bench.py --steps 3 "
-            "--warmup 1 --warm-seconds 0 --no-cpu-baseline --no-other-configs",
+# Profile sets: which bench invocation each rocprofv3 run wraps, and the file
+# name stem of its summaries under profiles/.
+PROFILE_SETS = {
+    "qwen2": dict(
+        stem="pasa_prefill_qwen2shape_s4096_decode_b64_kv8192", config="c2",
+        trace_args="--steps 20 --warmup 5 --no-cpu-baseline --no-other-configs",
+        pmc_args="--steps 3 --warmup 1 --warm-seconds 0 --no-cpu-baseline --no-other-configs",
+        prefill=K_PREFILL, decode=True),
+    "svd": dict(
+        stem="pasa_prefill_svdshape_b2_s9216_d64", config="c3",
+        trace_args="--profile-config c3 --steps 100",
+        pmc_args="--profile-config c3 --steps 3 --warm-seconds 0",
+        prefill=K_C3, decode=False),
+    "longctx": dict(
+        stem="pasa_prefill_longctx_s32768_h32_8_d128", config="c4",
+        trace_args="--profile-config c4 --steps 20",
+        pmc_args="--profile-config c4 --steps 2 --warm-seconds 0",
+        prefill=K_PREFILL, decode=False),
 }
+PMC_SETS = {
+    "pmc1": "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_VMEM "
+            "SQ_BUSY_CYCLES SQ_WAVE_CYCLES",
+    "pmc2": "SQ_LDS_BANK_CONFLICT SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
+            "SQ_WAIT_INST_LDS SQ_ACTIVE_INST_ANY SQ_WAIT_ANY GRBM_GUI_ACTIVE",
+    "fetch": "FETCH_SIZE",
+    "write": "WRITE_SIZE",
+}
+
+
+def profile_cmd(set_name, kind):
+    """The rocprofv3 command of one profile run (kind: trace, a PMC_SETS key,
+    or cfetch / cwrite for the copy calibration)."""
+    ps = PROFILE_SETS[set_name]
+    d = f"rocprof_out/{set_name}/{kind}"
+    if kind == "trace":
+        return (f"rocprofv3 --kernel-trace --stats -d {d} -o run --output-format csv "
+                f"-- python bench.py {ps['trace_args']}")
+    if kind in ("cfetch", "cwrite"):
+        c = "FETCH_SIZE" if kind == "cfetch" else "WRITE_SIZE"
+        return (f"rocprofv3 --pmc {c} -d {d} -o run --output-format csv "
+                f"-- python bench.py --calibrate-copy 1024")
+    return (f"rocprofv3 --pmc {PMC_SETS[kind]} -d {d} -o run --output-format csv "
+            f"-- python bench.py {ps['pmc_args']}")
 
 
 def source_hash():
@@ -83,24 +116,29 @@ def source_hash():
     return h.hexdigest()
 
 
-def recorded_traffic():
+def traffic_file(set_name):
+    return os.path.join(PROFILES, PROFILE_SETS[set_name]["stem"] + "_hbm_traffic.txt")
+
+
+def recorded_traffic(set_name="qwen2"):
     """(prefill_bytes, decode_bytes) per launch from the committed profile summary,
     or (None, None) if it is missing or was taken on other kernel sources."""
     try:
         kv = {}
-        for line in open(TRAFFIC_FILE):
+        for line in open(traffic_file(set_name)):
             if "=" in line and not line.startswith("#"):
                 a, b = line.split("=", 1)
                 kv[a.strip()] = b.strip()
         if kv.get("source_sha256") != source_hash():
             return None, None
-        return int(kv["prefill_traffic_bytes"]), int(kv["decode_split_traffic_bytes"])
+        dec = kv.get("decode_split_traffic_bytes")
+        return int(kv["prefill_traffic_bytes"]), (int(dec) if dec else None)
     except (OSError, KeyError, ValueError):
         return None, None
 
 
 def _counters(path):
-    """{kernel_substring: {counter: mean value per dispatch}} from a rocprofv3 csv."""
+    """{kernel name: {counter: mean value per dispatch}} from a rocprofv3 csv."""
     import csv
     import collections
     acc = collections.defaultdict(lambda: collections.defaultdict(list))
@@ -119,13 +157,14 @@ def _pick(table, sub):
     raise KeyError(sub)
 
 
-def summarize_profile(d):
+def summarize_profile(d, set_name):
     """Write the text summaries under profiles/ from a rocprofv3 output directory
-    laid out as PROFILE_CMDS produce it."""
+    laid out as profile_cmd() produces it (d/<kind>/run_*.csv)."""
     import csv
     import workloads as W
+    ps = PROFILE_SETS[set_name]
     os.makedirs(PROFILES, exist_ok=True)
-    wp, wd = W.CONFIGS["c2"], W.CONFIGS["c5"]
+    wp, wd = W.CONFIGS[ps["config"]], W.CONFIGS["c5"]
     stats = {r["Name"]: r for r in csv.DictReader(open(os.path.join(d, "trace", "run_kernel_stats.csv")))}
 
     def st(sub):
@@ -133,103 +172,119 @@ def summarize_profile(d):
             if sub in k:
                 return v
         raise KeyError(sub)
-    lines = ["# rocprofv3 kernel trace of bench.py: PASA prefill on the Qwen2-7B-shaped causal workload",
-             "# (batch 1, seq 4096, 28 query / 4 kv heads, head_dim 128) and split-KV decode on the decode",
-             "# workload (batch 64, kv length 8192, 28/4 heads, head_dim 128), one MI355X.",
-             "# command: " + PROFILE_CMDS["trace"],
+    title = {"c2": "the Qwen2-7B-shaped causal prefill (batch 1, seq 4096, 28 query / 4 kv heads, "
+                   "head_dim 128) and split-KV decode (batch 64, kv length 8192, 28/4 heads, head_dim 128)",
+             "c3": "the Stable-Video-Diffusion-shaped resonance prefill (batch 2, seq 9216, 5 heads, "
+                   "head_dim 64, non-causal)",
+             "c4": "the long-context causal prefill (batch 1, seq 32768, 32 query / 8 kv heads, "
+                   "head_dim 128)"}[ps["config"]]
+    lines = [f"# rocprofv3 kernel trace of bench.py on {title}, one MI355X.",
+             "# command: " + profile_cmd(set_name, "trace"),
              f"# kernel sources sha256: {source_hash()}",
              "kernel                         calls  avg_us    min_us    max_us   algorithmic    rate"]
-    pre = st(K_PREFILL)
+    pre = st(ps["prefill"])
     avg_p = float(pre["AverageNs"]) * 1e-3
     lines.append(f"pasa prefill                 {int(pre['Calls']):6d} {avg_p:8.2f} "
                  f"{float(pre['MinNs'])*1e-3:8.2f} {float(pre['MaxNs'])*1e-3:8.2f}  "
                  f"{wp.flops():.4e} flop  {wp.flops()/avg_p/1e6:8.1f} TFLOP/s "
                  f"({wp.flops()/avg_p/1e6/PEAK_FP16_TFLOPS:.3f} of 2500)")
-    sp = st(K_SPLIT)
-    avg_s = float(sp["AverageNs"]) * 1e-3
-    cb = st(K_COMBINE)
-    avg_c = float(cb["AverageNs"]) * 1e-3
-    lines.append(f"pasa decode split            {int(sp['Calls']):6d} {avg_s:8.2f} "
-                 f"{float(sp['MinNs'])*1e-3:8.2f} {float(sp['MaxNs'])*1e-3:8.2f}  "
-                 f"{wd.io_bytes():.4e} B     {wd.io_bytes()/avg_s/1e3:8.1f} GB/s "
-                 f"({wd.io_bytes()/avg_s/1e3/PEAK_HBM_GBPS:.3f} of 8000)")
-    lines.append(f"pasa decode combine          {int(cb['Calls']):6d} {avg_c:8.2f} "
-                 f"{float(cb['MinNs'])*1e-3:8.2f} {float(cb['MaxNs'])*1e-3:8.2f}")
-    for label, key in (("naive fp16 prefill", K_NAIVE), ("strict PASA prefill", K_STRICT)):
-        try:
-            kv = st(key)
-        except KeyError:
-            continue
-        lines.append(f"{label:<28} {int(kv['Calls']):6d} {float(kv['AverageNs'])*1e-3:8.2f} "
-                     f"{float(kv['MinNs'])*1e-3:8.2f} {float(kv['MaxNs'])*1e-3:8.2f}")
-    open(os.path.join(PROFILES, "pasa_prefill_qwen2shape_s4096_decode_b64_kv8192_kernel_trace.txt"), "w").write("\n".join(lines) + "\n")
+    if ps["decode"]:
+        sp = st(K_SPLIT)
+        avg_s = float(sp["AverageNs"]) * 1e-3
+        cb = st(K_COMBINE)
+        avg_c = float(cb["AverageNs"]) * 1e-3
+        lines.append(f"pasa decode split            {int(sp['Calls']):6d} {avg_s:8.2f} "
+                     f"{float(sp['MinNs'])*1e-3:8.2f} {float(sp['MaxNs'])*1e-3:8.2f}  "
+                     f"{wd.io_bytes():.4e} B     {wd.io_bytes()/avg_s/1e3:8.1f} GB/s "
+                     f"({wd.io_bytes()/avg_s/1e3/PEAK_HBM_GBPS:.3f} of 8000)")
+        lines.append(f"pasa decode combine          {int(cb['Calls']):6d} {avg_c:8.2f} "
+                     f"{float(cb['MinNs'])*1e-3:8.2f} {float(cb['MaxNs'])*1e-3:8.2f}")
+        for label, key in (("naive fp16 prefill", K_NAIVE), ("strict PASA prefill", K_STRICT)):
+            try:
+                kv = st(key)
+            except KeyError:
+                continue
+            lines.append(f"{label:<28} {int(kv['Calls']):6d} {float(kv['AverageNs'])*1e-3:8.2f} "
+                         f"{float(kv['MinNs'])*1e-3:8.2f} {float(kv['MaxNs'])*1e-3:8.2f}")
+    open(os.path.join(PROFILES, ps["stem"] + "_kernel_trace.txt"), "w").write("\n".join(lines) + "\n")
 
-    fetch = _counters(os.path.join(d, "fetch", "run_counter_collection.csv"))
-    write = _counters(os.path.join(d, "write", "run_counter_collection.csv"))
-    cfetch = _counters(os.path.join(d, "cfetch", "run_counter_collection.csv"))
-    cwrite = _counters(os.path.join(d, "cwrite", "run_counter_collection.csv"))
-    copy_bytes = 1024 * (1 << 20)
-    cf = _pick(cfetch, "copyBuffer")["FETCH_SIZE"] * 1024
-    cw = _pick(cwrite, "copyBuffer")["WRITE_SIZE"] * 1024
-    ff, wf = copy_bytes / cf, copy_bytes / cw
-    pf = _pick(fetch, K_PREFILL)["FETCH_SIZE"]
-    pw = _pick(write, K_PREFILL)["WRITE_SIZE"]
-    sf = _pick(fetch, K_SPLIT)["FETCH_SIZE"]
-    sw = _pick(write, K_SPLIT)["WRITE_SIZE"]
-    p_bytes = int(pf * 1024 * ff + pw * 1024 * wf)
-    s_bytes = int(sf * 1024 * ff + sw * 1024 * wf)
-    t = ["# HBM traffic per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),",
-         "# each scaled by what the same counter reads for a plain 1 GiB device-to-device copy.",
-         "# commands:",
-         "#   " + PROFILE_CMDS["fetch"], "#   " + PROFILE_CMDS["write"],
-         "#   " + PROFILE_CMDS["cfetch"], "#   " + PROFILE_CMDS["cwrite"],
-         f"source_sha256={source_hash()}",
-         f"copy_bytes={copy_bytes}",
-         f"copy_fetch_kib={cf/1024:.1f}", f"copy_write_kib={cw/1024:.1f}",
-         f"fetch_factor={ff:.4f}", f"write_factor={wf:.4f}",
-         f"prefill_fetch_kib={pf:.1f}", f"prefill_write_kib={pw:.1f}",
-         f"prefill_traffic_bytes={p_bytes}",
-         f"prefill_algorithmic_bytes={wp.io_bytes()}",
-         f"decode_split_fetch_kib={sf:.1f}", f"decode_split_write_kib={sw:.1f}",
-         f"decode_split_traffic_bytes={s_bytes}",
-         f"decode_algorithmic_bytes={wd.io_bytes()}"]
-    open(TRAFFIC_FILE, "w").write("\n".join(t) + "\n")
+    t = []
+    fp = os.path.join(d, "fetch", "run_counter_collection.csv")
+    if os.path.exists(fp):
+        fetch = _counters(fp)
+        write = _counters(os.path.join(d, "write", "run_counter_collection.csv"))
+        # the copy calibration is taken once (under the qwen2 set) and reused
+        cal = d if os.path.exists(os.path.join(d, "cfetch")) else os.path.join(os.path.dirname(d), "qwen2")
+        cfetch = _counters(os.path.join(cal, "cfetch", "run_counter_collection.csv"))
+        cwrite = _counters(os.path.join(cal, "cwrite", "run_counter_collection.csv"))
+        copy_bytes = 1024 * (1 << 20)
+        cf = _pick(cfetch, "copyBuffer")["FETCH_SIZE"] * 1024
+        cw = _pick(cwrite, "copyBuffer")["WRITE_SIZE"] * 1024
+        ff, wf = copy_bytes / cf, copy_bytes / cw
+        pf = _pick(fetch, ps["prefill"])["FETCH_SIZE"]
+        pw = _pick(write, ps["prefill"])["WRITE_SIZE"]
+        p_bytes = int(pf * 1024 * ff + pw * 1024 * wf)
+        t = ["# HBM traffic per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),",
+             "# each scaled by what the same counter reads for a plain 1 GiB device-to-device copy.",
+             "# commands:",
+             "#   " + profile_cmd(set_name, "fetch"), "#   " + profile_cmd(set_name, "write"),
+             "#   " + profile_cmd("qwen2", "cfetch"), "#   " + profile_cmd("qwen2", "cwrite"),
+             f"source_sha256={source_hash()}",
+             f"copy_bytes={copy_bytes}",
+             f"copy_fetch_kib={cf/1024:.1f}", f"copy_write_kib={cw/1024:.1f}",
+             f"fetch_factor={ff:.4f}", f"write_factor={wf:.4f}",
+             f"prefill_fetch_kib={pf:.1f}", f"prefill_write_kib={pw:.1f}",
+             f"prefill_traffic_bytes={p_bytes}",
+             f"prefill_algorithmic_bytes={wp.io_bytes()}"]
+        if ps["decode"]:
+            sf = _pick(fetch, K_SPLIT)["FETCH_SIZE"]
+            sw = _pick(write, K_SPLIT)["WRITE_SIZE"]
+            s_bytes = int(sf * 1024 * ff + sw * 1024 * wf)
+            t += [f"decode_split_fetch_kib={sf:.1f}", f"decode_split_write_kib={sw:.1f}",
+                  f"decode_split_traffic_bytes={s_bytes}",
+                  f"decode_algorithmic_bytes={wd.io_bytes()}"]
+        open(traffic_file(set_name), "w").write("\n".join(t) + "\n")
 
     rows = []
-    for key, title in (("pmc1", "instruction counts"), ("pmc2", "busy / wait cycles")):
+    for key, title2 in (("pmc1", "instruction counts"), ("pmc2", "busy / wait cycles")):
         path = os.path.join(d, key, "run_counter_collection.csv")
         if not os.path.exists(path):
             continue
         c = _counters(path)
-        rows.append(f"# {title}: " + PROFILE_CMDS[key])
-        for name, sub in (("pasa prefill", K_PREFILL), ("pasa decode split", K_SPLIT)):
+        rows.append(f"# {title2}: " + profile_cmd(set_name, key))
+        kernels = [("pasa prefill", ps["prefill"])] + ([("pasa decode split", K_SPLIT)] if ps["decode"] else [])
+        for name, sub in kernels:
             vals = _pick(c, sub)
             rows.append(f"{name}: " + ", ".join(f"{k}={v:.0f}" for k, v in sorted(vals.items())))
     if rows:
-        open(os.path.join(PROFILES, "pasa_prefill_qwen2shape_s4096_decode_b64_kv8192_counters.txt"), "w").write("\n".join(rows) + "\n")
-    print("\n".join(lines + t))
+        rows.append(f"# kernel sources sha256: {source_hash()}")
+        open(os.path.join(PROFILES, ps["stem"] + "_counters.txt"), "w").write("\n".join(rows) + "\n")
+    print("\n".join(lines + t + rows))
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=5,
+                    help="at least this many untimed warmup steps (more run until --warm-seconds)")
     ap.add_argument("--warm-seconds", type=float, default=0.3,
                     help="keep running warmup steps until this much wall time has passed "
                          "(the GPU clock ramps up over the first ~40 ms of sustained load)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
-                    help="skip the oracle timing and the sampled parity check")
+                    help="skip the oracle timing and the sampled parity checks")
     ap.add_argument("--no-other-configs", action="store_true",
-                    help="skip the latency / throughput lines of the other prefill configs "
-                         "(c1, c3, c4); profiling runs use this so that the c2 kernel's "
-                         "averages are its own")
+                    help="skip the other prefill workloads (c1, c3, c4), the paged and e4m3 "
+                         "variants and the peak microbenchmarks; profiling runs use this so "
+                         "that the c2 kernel's averages are its own")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--summarize-profile", metavar="DIR", default=None,
+    ap.add_argument("--profile-config", choices=("c3", "c4"), default=None,
+                    help="run only this prefill workload: --steps launches after the warmup")
+    ap.add_argument("--summarize-profile", nargs=2, metavar=("DIR", "SET"), default=None,
                     help="write the text summaries under profiles/ from a rocprofv3 output "
-                         "directory (subdirectories trace, fetch, write, cfetch, cwrite, pmc1, "
-                         "pmc2 made by the commands recorded in those summaries), then exit")
+                         "directory (subdirectories trace, fetch, write, pmc1, pmc2, and for the "
+                         "qwen2 set cfetch, cwrite, made by profile_cmd()), then exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times "
                          "(reference for the HBM byte counters), then exit")
@@ -247,6 +302,110 @@ def calibrate_copy(mib):
     print(json.dumps({"copy_bytes_per_launch": mib * (1 << 20)}), flush=True)
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def warm(fn, seconds, min_iters=1):
+    """Run fn back to back until min_iters calls and `seconds` of wall time:
+    the GPU raises its clock only after tens of milliseconds of sustained
+    load, so timings taken right after an idle spell measure the ramp.
+    Returns (calls, seconds)."""
+    import torch
+    t = time.perf_counter()
+    i = 0
+    while i < min_iters or time.perf_counter() - t < seconds:
+        for _ in range(min(8, max(1, min_iters - i)) if seconds <= 0 else 8):
+            fn()
+            i += 1
+        torch.cuda.synchronize()
+    return i, time.perf_counter() - t
+
+
+def timed_batches(fn, reps, batches, stream):
+    """Median and min over `batches` runs of `reps` back-to-back calls, each run
+    bracketed by events on the launch stream (ms per call)."""
+    import torch
+    ts = []
+    for _ in range(batches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / reps)
+    ts.sort()
+    return ts[len(ts) // 2], ts[0]
+
+
+def measure_peaks(stream):
+    """Achievable peaks on this GPU: fp16 matrix-core TFLOP/s (back-to-back
+    v_mfma_f32_32x32x16_f16, four chains per wave, four waves per SIMD) and HBM
+    read GB/s (a non-temporal 16-byte streaming read of 4 GiB)."""
+    import ctypes
+    import torch
+    if not os.path.exists(PEAK_LIB):
+        return None
+    lib = ctypes.CDLL(PEAK_LIB)
+    lib.peak_mfma_f16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int,
+                                  ctypes.c_void_p]
+    s = ctypes.c_void_p(stream.cuda_stream)
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 4 * n_cu, 2048          # 4 workgroups of 4 waves per CU
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+
+    def mfma():
+        assert lib.peak_mfma_f16(out.data_ptr(), blocks, iters, s) == 0
+    warm(mfma, 0.1)
+    med, _ = timed_batches(mfma, 3, 5, stream)
+    flops = blocks * 4 * 4 * iters * 32768.0
+    nbytes = 4 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    hblocks = 8 * n_cu
+    hout = torch.empty(hblocks * 256, dtype=torch.int32, device="cuda")
+
+    def hbm():
+        assert lib.peak_hbm_read(src.data_ptr(), nbytes // 16, hout.data_ptr(), hblocks, s) == 0
+    warm(hbm, 0.1)
+    hmed, _ = timed_batches(hbm, 3, 5, stream)
+    del src, hout, out
+    torch.cuda.empty_cache()
+    return {"mfma_f16_tflops": round(flops / (med * 1e-3) / 1e12, 1),
+            "hbm_read_gbps": round(nbytes / (hmed * 1e-3) / 1e9, 1),
+            "how": "fp16 32x32x16 matrix products back to back (4 chains per wave, 16 waves per CU); "
+                   "non-temporal 16-byte streaming read of 4 GiB"}
+
+
+def profile_only(args):
+    """--profile-config: one prefill workload alone, --steps launches after the
+    warmup, for rocprofv3 runs of that workload."""
+    import torch
+    import precision_flashattention_numerics_amd as pasa
+    import workloads as W
+    w = W.CONFIGS[args.profile_config]
+    tq, tk, tv = (torch.from_numpy(x).cuda() for x in W.generate(w))
+    o = torch.empty_like(tq)
+    lse = torch.empty((w.batch, w.heads_q, w.seqlen_q), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        pasa.attn_fwd(tq, tk, tv, causal=w.causal, scale=w.scale, out=o, lse=lse)
+    n_warm, s_warm = warm(fwd, args.warm_seconds, args.warmup)
+    med, mn = timed_batches(fwd, args.steps, 1, stream)
+    tf = w.flops() / (med * 1e-3) / 1e12
+    print(json.dumps({"config": w.name, "launches": args.steps, "ms": round(med, 5),
+                      "tflops": round(tf, 2), "frac": round(tf / PEAK_FP16_TFLOPS, 4),
+                      "warmup_launches": n_warm, "warmup_seconds": round(s_warm, 3)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -258,7 +417,10 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
     if args.summarize_profile:
-        summarize_profile(args.summarize_profile)
+        summarize_profile(*args.summarize_profile)
+        return
+    if args.profile_config:
+        profile_only(args)
         return
 
     import numpy as np
@@ -293,19 +455,6 @@ def main():
         pasa.attn_decode(tqd, tkd, tvd, scale=wd.scale, out=od, lse=ld, workspace=ws,
                          num_splits=nsplit)
 
-    def warm(fn, seconds, min_iters=1):
-        """Run fn back to back until min_iters calls and `seconds` of wall time:
-        the GPU raises its clock only after tens of milliseconds of sustained
-        load, so timings taken right after an idle spell measure the ramp."""
-        t = time.perf_counter()
-        i = 0
-        while i < min_iters or time.perf_counter() - t < seconds:
-            for _ in range(8):
-                fn()
-            i += 8
-            torch.cuda.synchronize()
-        return i
-
     def step():
         prefill()
         decode()
@@ -320,8 +469,8 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     cold_ms = e0.elapsed_time(e1) / 5
-    n_warm = warm(step, args.warm_seconds, args.warmup)
-    log(f"warmup {n_warm} steps ({args.warm_seconds} s) ...")
+    n_warm, s_warm = warm(step, args.warm_seconds, args.warmup)
+    log(f"warmup {n_warm} steps ({s_warm:.2f} s) ...")
 
     # K steps: the K prefill launches back to back, then the K decode launches,
     # each run bracketed by events on the launch stream, so that a kernel's
@@ -344,21 +493,32 @@ def main():
     dec_avg = ev[1].elapsed_time(ev[2]) / K
     log(f"timed {K} steps: prefill {pre_avg:.4f} ms, decode {dec_avg:.4f} ms, wall {wall:.3f} s")
 
-    traffic_p, traffic_d = recorded_traffic()
+    traffic_p, traffic_d = recorded_traffic("qwen2")
     flops = wp.flops()
     tflops = flops / (pre_avg * 1e-3) / 1e12
     dec_bytes = wd.io_bytes()
     dec_gbps = dec_bytes / (dec_avg * 1e-3) / 1e9
 
-    # parity of the benchmarked outputs on sampled rows, and the naive kernel
     out = {}
     o_np = op.cpu().numpy()
     l_np = lp.cpu().numpy()
     od_np = od.cpu().numpy()
     out["pasa_nonfinite"] = nonfinite(o_np) + nonfinite(od_np)
-    on, _ = pasa.naive_attn_fwd(tqp, tkp, tvp, causal=wp.causal, scale=wp.scale)
-    torch.cuda.synchronize()
-    out["naive_nonfinite"] = nonfinite(on.cpu().numpy())
+
+    def naive_report(tq, tk, tv, w):
+        """The naive fp16 kernel on the same input: inf/NaN outputs, and which
+        heads have any (the overflow PASA avoids)."""
+        on, _ = pasa.naive_attn_fwd(tq, tk, tv, causal=w.causal, scale=w.scale)
+        torch.cuda.synchronize()
+        on = on.cpu().numpy()
+        per_head = [nonfinite(on[:, :, h]) for h in range(w.heads_q)]
+        rep = {"nonfinite": int(sum(per_head)), "of": int(on.size),
+               "heads_nonfinite": int(sum(1 for x in per_head if x)), "heads": w.heads_q}
+        return rep, on, [h for h in range(w.heads_q) if per_head[h] == 0]
+
+    naive = {}
+    naive["c2"], _, _ = naive_report(tqp, tkp, tvp, wp)
+    out["naive_nonfinite"] = naive["c2"]["nonfinite"]
     # the variant with fp16 running maximum and offset: its error is reported
     # beside the default's (and its speed, outside the timed steps)
     os_, ls_ = pasa.attn_fwd_strict(tqp, tkp, tvp, causal=wp.causal, scale=wp.scale)
@@ -366,58 +526,58 @@ def main():
     def strict():
         pasa.attn_fwd_strict(tqp, tkp, tvp, causal=wp.causal, scale=wp.scale, out=os_, lse=ls_)
     warm(strict, 0.1)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(K):
-        strict()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    out["strict_tflops"] = round(flops / (e0.elapsed_time(e1) / K * 1e-3) / 1e12, 3)
+    med, _ = timed_batches(strict, K, 1, stream)
+    out["strict_tflops"] = round(flops / (med * 1e-3) / 1e12, 3)
     os_np, ls_np = os_.cpu().numpy(), ls_.cpu().numpy()
     out["strict_nonfinite"] = nonfinite(os_np)
 
     # the other prefill configs, outside the timed steps: c1 is launch-bound
     # (its latency is reported), c3 and c4 against the same MFMA peak
+    kept = {}      # inputs and sampled outputs for the oracle leg
+    peaks = None
     if not args.no_other_configs:
         other = {}
         for name, reps in (("c1", 20), ("c3", 10), ("c4", 2)):
             w = W.CONFIGS[name]
             log(f"config {name} ...")
-            tq, tk, tv = (torch.from_numpy(x).cuda() for x in W.generate(w))
+            q_, k_, v_ = W.generate(w)
+            tq, tk, tv = (torch.from_numpy(x).cuda() for x in (q_, k_, v_))
             o2 = torch.empty_like(tq)
             l2 = torch.empty((w.batch, w.heads_q, w.seqlen_q), dtype=torch.float32, device="cuda")
+
             def fwd2():
                 pasa.attn_fwd(tq, tk, tv, causal=w.causal, scale=w.scale, out=o2, lse=l2)
-            ts = []
             if name == "c1":
                 # launch-bound: the latency of single launches
-                for _ in range(2):
-                    fwd2()
-                for _ in range(reps):
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    fwd2()
-                    e1.record(stream)
-                    torch.cuda.synchronize()
-                    ts.append(e0.elapsed_time(e1))
+                warm(fwd2, 0.0, 2)
+                ts = sorted(timed_batches(fwd2, 1, 1, stream)[0] for _ in range(reps))
+                med, mn = ts[len(ts) // 2], ts[0]
             else:
                 # throughput: warm, then batches of back-to-back launches
                 warm(fwd2, 0.15)
-                for _ in range(5):
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    for _ in range(reps):
-                        fwd2()
-                    e1.record(stream)
-                    torch.cuda.synchronize()
-                    ts.append(e0.elapsed_time(e1) / reps)
-            ts.sort()
-            med = ts[len(ts) // 2]
+                med, mn = timed_batches(fwd2, reps, 5, stream)
             tf = w.flops() / (med * 1e-3) / 1e12
-            other[name] = {"median_ms": round(med, 5), "min_ms": round(ts[0], 5),
-                           "tflops": round(tf, 2), "frac": round(tf / 2500.0, 4),
-                           "nonfinite": nonfinite(o2.cpu().numpy())}
-            del tq, tk, tv, o2, l2
+            o2_np = o2.cpu().numpy()
+            other[name] = {"median_ms": round(med, 5), "min_ms": round(mn, 5),
+                           "tflops": round(tf, 2), "frac": round(tf / PEAK_FP16_TFLOPS, 4),
+                           "nonfinite": nonfinite(o2_np)}
+            if name != "c1":
+                naive[name], on, fin_heads = naive_report(tq, tk, tv, w)
+                rng = np.random.default_rng(7)
+                rows = np.sort(rng.choice(w.batch * w.heads_q * w.seqlen_q, 256, replace=False))
+                b, rem = np.divmod(rows, w.heads_q * w.seqlen_q)
+                h, i = np.divmod(rem, w.seqlen_q)
+                keep = dict(w=w, q=q_, k=k_, v=v_, rows=rows, o=o2_np[b, i, h])
+                if fin_heads:
+                    nrows = np.concatenate([
+                        np.sort(rng.choice(w.seqlen_q, 64, replace=False)) + (bb * w.heads_q + hh) * w.seqlen_q
+                        for bb in range(w.batch) for hh in fin_heads]).astype(np.int64)
+                    b, rem = np.divmod(nrows, w.heads_q * w.seqlen_q)
+                    h, i = np.divmod(rem, w.seqlen_q)
+                    keep.update(naive_rows=nrows, naive_o=on[b, i, h])
+                kept[name] = keep
+                del on
+            del tq, tk, tv, o2, l2, o2_np
             torch.cuda.empty_cache()
         # the decode workload over a paged cache: 64-key pages scattered over
         # the pool in a seeded random order (HBM-bound like the contiguous one)
@@ -435,13 +595,7 @@ def main():
         def paged():
             pasa.attn_decode_paged(tqd, kpool, vpool, table, lens, scale=wd.scale, out=opg, lse=lpg)
         warm(paged, 0.1)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(10):
-            paged()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        pg_ms = e0.elapsed_time(e1) / 10
+        pg_ms, _ = timed_batches(paged, 10, 1, stream)
         other["c5_paged64"] = {"ms": round(pg_ms, 5),
                                "GBps": round(wd.io_bytes() / (pg_ms * 1e-3) / 1e9, 1),
                                "frac": round(wd.io_bytes() / (pg_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
@@ -458,18 +612,16 @@ def main():
         def fp8():
             pasa.attn_fwd_fp8(q8, k8, tvp, q8s, k8s, causal=wp.causal, scale=wp.scale, out=o8, lse=l8)
         warm(fp8, 0.1)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(10):
-            fp8()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        f8_ms = e0.elapsed_time(e1) / 10
+        f8_ms, _ = timed_batches(fp8, 10, 1, stream)
         other["c2_fp8_qk"] = {"ms": round(f8_ms, 5),
                               "tflops": round(flops / (f8_ms * 1e-3) / 1e12, 2),
                               "nonfinite": nonfinite(o8.cpu().numpy())}
         del q8, k8, o8, l8
+        torch.cuda.empty_cache()
         out["other_configs"] = other
+        log("peak microbenchmarks ...")
+        peaks = measure_peaks(stream)
+    out["naive"] = naive
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -505,21 +657,41 @@ def main():
         out["lse_max_abs_err_sampled"] = float(np.max(np.abs(l_np[b, h, i] - rl)))
         out["strict_rel_rmse_sampled"] = rel_rmse(os_np[b, i, h], ro)
         out["strict_lse_max_abs_err_sampled"] = float(np.max(np.abs(ls_np[b, h, i] - rl)))
+        # the other workloads' sampled rows, and the naive kernel's error on
+        # the heads where it stayed finite
+        for name, kp_ in kept.items():
+            w = kp_["w"]
+            r_o, _ = attn_fp64(kp_["q"], kp_["k"], kp_["v"], w.scale, w.causal, rows=kp_["rows"])
+            out["other_configs"][name]["rel_rmse_sampled"] = rel_rmse(kp_["o"], r_o)
+            if "naive_rows" in kp_:
+                r_n, _ = attn_fp64(kp_["q"], kp_["k"], kp_["v"], w.scale, w.causal,
+                                   rows=kp_["naive_rows"])
+                naive[name]["finite_heads_rel_rmse_sampled"] = rel_rmse(kp_["naive_o"], r_n)
         cpu = {"value": cpu_flops / tc / 1e12, "unit": "TFLOP/s", "cores": num_threads(),
-               "kind": "oracle",
+               "cpu_model": cpu_model(), "kind": "oracle",
                "sample": (f"{'all ' if n_rows == total_rows else ''}{n_rows} "
                           f"{'' if n_rows == total_rows else 'random '}query rows of the prefill "
                           f"workload ({cpu_flops:.3e} algorithmic flops, binary64, OpenMP), "
                           f"median of {len(times)} runs over {sum(times):.1f} s: {tc:.2f} s per run")}
         log(f"oracle: {n_rows} rows, {len(times)} runs, median {tc:.2f} s")
 
+    roof = {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP16_TFLOPS, 4), "traffic": traffic_p}
+    roof_d = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+              "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic_d}
+    if peaks:
+        roof["measured_peak"] = peaks["mfma_f16_tflops"]
+        roof["frac_of_measured_peak"] = round(tflops / peaks["mfma_f16_tflops"], 4)
+        roof_d["measured_peak"] = peaks["hbm_read_gbps"]
+        roof_d["frac_of_measured_peak"] = round(dec_gbps / peaks["hbm_read_gbps"], 4)
     line = {
         "metric": "PASA fwd TFLOP/s (fraction of fp16 MFMA peak); decode HBM GB/s; RMSE vs fp64",
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": n_warm,
+        "warmup_seconds": round(s_warm, 3),
         "ms_per_step": round(wall * 1e3 / K, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -535,16 +707,12 @@ def main():
                               "splits": nsplit, "bias": 30}},
         "prefill_ms": round(pre_avg, 5),
         "prefill_ms_cold": round(cold_ms, 5),
-        "warm_seconds": args.warm_seconds,
         "prefill_frac_of_peak": round(tflops / PEAK_FP16_TFLOPS, 4),
         "decode_ms": round(dec_avg, 5),
         "decode_GBps": round(dec_gbps, 1),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_FP16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP16_TFLOPS, 4),
-                     "traffic": traffic_p},
-        "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps, 1),
-                            "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                            "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": traffic_d},
+        "roofline": roof,
+        "roofline_decode": roof_d,
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
         **out,
     }

@@ -30,7 +30,8 @@
  *    query i iff j <= i + seqlen_kv - seqlen_q.
  *  - On any error nothing is enqueued and no output byte is written.
  *  - Supported: head_dim 64 or 128; num_heads_q % gqa_group == 0; any
- *    batch >= 1 and sequence lengths >= 1 (ragged tails are masked).
+ *    batch >= 1 and sequence lengths from 1 to 2^31 - 512 (ragged tails are
+ *    masked), within the per-call limits each entry point lists.
  *    seqlen_kv <= 65504 for pasa_attn_fwd and pasa_naive_attn_fwd, because the
  *    running softmax sum is carried in fp16; the split-KV decode path has no
  *    such bound (each split's sum is at most 65504 keys; the combine is fp32).

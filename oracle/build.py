@@ -10,16 +10,24 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=undefined"]
+
+
+def build(verbose: bool = False, sanitize: bool = False, out: str = None) -> str:
+    """Build liboracle.so; with sanitize=True an address- and
+    undefined-behaviour-sanitized copy (to `out`) for the CPU sanitizer test."""
     src = os.path.join(HERE, "oracle.c")
-    tmp = LIB + ".tmp"
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+    lib = out or LIB
+    tmp = lib + ".tmp"
+    opt = SANITIZE_FLAGS if sanitize else ["-O2"]
+    cmd = ["gcc", *opt, "-fopenmp", "-fPIC", "-shared", "-std=c11",
            "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -9,7 +9,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# PASA_ORACLE_LIB selects another build of the same source (the sanitized one
+# the CPU sanitizer test makes)
+_LIB_PATH = os.environ.get("PASA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)

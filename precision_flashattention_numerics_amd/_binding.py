@@ -115,16 +115,11 @@ def _fwd(fn, where, q, k, v, causal, scale, out, lse, return_lse, stream):
         scale = D ** -0.5
     if out is None:
         out = torch.empty_like(q)
-    else:
-        _want(out, "out")
-        if out.shape != q.shape:
-            raise ValueError("out must have q's shape")
+    _want_shape(out, "out", q.shape, torch.float16)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     if lse is not None:
-        _want(lse, "lse", torch.float32)
-        if tuple(lse.shape) != (B, Hq, Sq):
-            raise ValueError("lse must be [B,Hq,Sq]")
+        _want_shape(lse, "lse", (B, Hq, Sq), torch.float32)
     rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Skv, Hq, Hq // Hkv, D,
             float(scale), int(bool(causal)), _stream(stream))
     _check(rc, where)
@@ -162,8 +157,11 @@ def attn_fwd_fp8(q8, k8, v, q_scale, k_scale, causal=False, scale=None, out=None
         scale = D ** -0.5
     if out is None:
         out = torch.empty(q8.shape, dtype=torch.float16, device=q8.device)
+    _want_shape(out, "out", q8.shape, torch.float16)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
+    if lse is not None:
+        _want_shape(lse, "lse", (B, Hq, Sq), torch.float32)
     rc = _lib.pasa_attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v), _ptr(out), _ptr(lse), B, Sq, Skv, Hq,
                                 Hq // Hkv, D, float(scale), float(q_scale), float(k_scale),
                                 int(bool(causal)), _stream(stream))

@@ -410,7 +410,7 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     auto kern = fwd_kernel<D, CAUSAL, VAR, KS>;
     static_assert((KS ? 2 : 1) * fwd_smem_bytes<D>() <= 160 * 1024, "LDS of one CU");
     constexpr int rows = KS ? kBR / 2 : kBR;
-    const int n_qtiles = (a.seqlen_q + rows - 1) / rows;
+    const int n_qtiles = (int)(((int64_t)a.seqlen_q + rows - 1) / rows);   // item count checked by the ABI
     const int64_t n_items = (int64_t)a.batch * a.num_heads_q * n_qtiles;
     hipLaunchKernelGGL(kern, dim3((unsigned)n_items), dim3(kThreads), 0, stream,
                        (const _Float16*)a.q, (const _Float16*)a.k, (const _Float16*)a.v,
@@ -430,8 +430,8 @@ bool use_key_split(const FwdArgs& a) {
         n_cu < 1)
         return false;
     const int64_t heads = (int64_t)a.batch * a.num_heads_q;
-    const int64_t n256 = heads * ((a.seqlen_q + kBR - 1) / kBR);
-    const int64_t n128 = heads * ((a.seqlen_q + kBR / 2 - 1) / (kBR / 2));
+    const int64_t n256 = heads * (((int64_t)a.seqlen_q + kBR - 1) / kBR);
+    const int64_t n128 = heads * (((int64_t)a.seqlen_q + kBR / 2 - 1) / (kBR / 2));
     if (n128 > 0x7FFFFFFFLL) return false;
     return (n128 + n_cu - 1) / n_cu < 2 * ((n256 + n_cu - 1) / n_cu);
 }

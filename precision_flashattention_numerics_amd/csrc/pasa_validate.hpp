@@ -1,0 +1,180 @@
+// Argument validation of the C ABI (include/pasa_attn.h): every check an entry
+// point makes before it enqueues anything.  Plain host C++ with no device code
+// and no HIP runtime calls, so that it can also be compiled on its own (with the
+// host compiler and its sanitizers) and driven with edge-case sizes.
+#pragma once
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pasa_attn.h"
+
+namespace pasa {
+namespace validate {
+
+constexpr int kDecodeBlock = 32;         // keys per decode sub-tile; splits are whole sub-tiles
+constexpr int kMaxFp16Sum = 65504;       // keys one fp16 running sum may hold
+constexpr int kFwdRows = 256;            // query rows per prefill work item (at most)
+// Longest sequence: the kernels index rows as int, and a work item's last row
+// (its first row + 255) must not overflow.
+constexpr int kMaxSeq = 0x7FFFFFFF - 511;
+
+inline bool supported_dim(int d) { return d == 64 || d == 128; }
+
+// Element counts must stay below 2^62 so 64-bit indexing cannot overflow.
+inline bool fits(int64_t a, int64_t b, int64_t c, int64_t d) {
+    const double p = (double)a * (double)b * (double)c * (double)d;
+    return p < 4.0e18;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Checks shared by the forward and decode entry points.
+inline int common(const void* q, const void* k, const void* v, const void* o, int batch,
+                  int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group, int head_dim,
+                  float softmax_scale) {
+    if (!q || !k || !v || !o) return PASA_ERR_INVALID;
+    if (batch < 1 || seqlen_q < 1 || seqlen_kv < 1 || num_heads_q < 1 || gqa_group < 1 ||
+        head_dim < 1)
+        return PASA_ERR_INVALID;
+    if (num_heads_q % gqa_group != 0) return PASA_ERR_INVALID;
+    if (!supported_dim(head_dim)) return PASA_ERR_UNSUPPORTED;
+    if (seqlen_q > kMaxSeq || seqlen_kv > kMaxSeq) return PASA_ERR_UNSUPPORTED;
+    if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return PASA_ERR_UNSUPPORTED;
+    if (!fits(batch, seqlen_q, num_heads_q, head_dim) ||
+        !fits(batch, seqlen_kv, num_heads_q, head_dim))
+        return PASA_ERR_UNSUPPORTED;
+    // one head's K/V slab of one sequence is addressed through a buffer
+    // descriptor: 32-bit byte offsets
+    if ((int64_t)seqlen_kv * (num_heads_q / gqa_group) * head_dim * 2 > 0xFFFFFFFFLL)
+        return PASA_ERR_UNSUPPORTED;
+    return PASA_OK;
+}
+
+// pasa_attn_fwd and its variants.
+inline int fwd(const void* q, const void* k, const void* v, const void* o, int batch,
+               int seqlen_q, int seqlen_kv, int num_heads_q, int gqa_group, int head_dim,
+               float softmax_scale, int causal) {
+    const int rc = common(q, k, v, o, batch, seqlen_q, seqlen_kv, num_heads_q, gqa_group, head_dim,
+                          softmax_scale);
+    if (rc != PASA_OK) return rc;
+    if (causal != 0 && causal != 1) return PASA_ERR_INVALID;
+    if (seqlen_kv > kMaxFp16Sum) return PASA_ERR_UNSUPPORTED;
+    // the prefill's work items (up to 256 query rows of one head) are counted in int
+    if ((int64_t)batch * num_heads_q * (((int64_t)seqlen_q + kFwdRows - 1) / kFwdRows) >
+        0x7FFFFFFFLL)
+        return PASA_ERR_UNSUPPORTED;
+    return PASA_OK;
+}
+
+// The dequantisation scales of pasa_attn_fwd_fp8.
+inline int fp8_scales(float q_scale, float k_scale, float softmax_scale) {
+    if (!(q_scale > 0.0f) || !isfinite(q_scale) || !(k_scale > 0.0f) || !isfinite(k_scale))
+        return PASA_ERR_UNSUPPORTED;
+    const float dq = q_scale * k_scale;
+    if (!(dq > 0.0f) || !isfinite(dq) || !isfinite(softmax_scale * dq)) return PASA_ERR_UNSUPPORTED;
+    return PASA_OK;
+}
+
+// pasa_attn_decode_splits: waves on 256 CUs, measured: at head_dim 128 two
+// per CU (LDS would hold three, but fewer and longer key streams per sequence
+// read the cache faster); at head_dim 64 three per CU (of the six LDS holds).
+inline int decode_splits(int batch, int seqlen_kv, int num_heads_q, int gqa_group, int head_dim) {
+    if (batch < 1 || seqlen_kv < 1 || num_heads_q < 1 || gqa_group < 1 ||
+        num_heads_q % gqa_group != 0 || (head_dim != 64 && head_dim != 128))
+        return 0;
+    const int64_t units = (int64_t)batch * (num_heads_q / gqa_group) * ((gqa_group + 31) / 32);
+    const int64_t target = head_dim == 64 ? 768 : 512;
+    int64_t n = (target + units - 1) / units;
+    const int64_t blocks = ((int64_t)seqlen_kv + kDecodeBlock - 1) / kDecodeBlock;
+    if (n > blocks) n = blocks;
+    if (n > 65535) n = 65535;
+    return (int)(n < 1 ? 1 : n);
+}
+
+inline size_t workspace_bytes(int batch, int num_heads_q, int head_dim, int num_splits) {
+    if (batch < 1 || num_heads_q < 1 || head_dim < 1 || num_splits < 1) return 0;
+    const size_t rows = (size_t)batch * num_heads_q * num_splits;
+    return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+// The decode launches one wave per (sequence, key/value head, chunk of 32
+// query heads, split) and one combine workgroup per (sequence, query head),
+// each a 1-D grid indexed by int.
+inline bool decode_grids_fit(int batch, int num_heads_q, int gqa_group, int n) {
+    const int64_t waves = (int64_t)batch * (num_heads_q / gqa_group) * ((gqa_group + 31) / 32) * n;
+    return waves <= 0x7FFFFFFFLL && (int64_t)batch * num_heads_q <= 0x7FFFFFFFLL;
+}
+
+// The split count a decode call uses (num_splits, or the library's choice for
+// 0, clamped to the number of 32-key sub-tiles), and the checks on it.  On
+// success *n_used holds the count.
+inline int decode_split_count(int batch, int seqlen_kv, int num_heads_q, int gqa_group,
+                              int head_dim, int num_splits, int* n_used) {
+    if (num_splits < 0) return PASA_ERR_INVALID;
+    int n = num_splits == 0 ? decode_splits(batch, seqlen_kv, num_heads_q, gqa_group, head_dim)
+                            : num_splits;
+    const int blocks = (int)(((int64_t)seqlen_kv + kDecodeBlock - 1) / kDecodeBlock);
+    if (n > blocks) n = blocks;
+    if (n < 1 || n > 65535 || !decode_grids_fit(batch, num_heads_q, gqa_group, n))
+        return PASA_ERR_UNSUPPORTED;
+    // every split sums at most 65504 keys in fp16
+    const int64_t per_split = ((int64_t)blocks + n - 1) / n * kDecodeBlock;
+    if (per_split > kMaxFp16Sum) return PASA_ERR_UNSUPPORTED;
+    *n_used = n;
+    return PASA_OK;
+}
+
+// A caller's decode workspace for n splits: present, 256-byte aligned, large enough.
+inline int decode_workspace(const void* workspace, size_t workspace_bytes_given, int batch,
+                            int num_heads_q, int head_dim, int n) {
+    const size_t need = workspace_bytes(batch, num_heads_q, head_dim, n);
+    if (workspace == nullptr || ((uintptr_t)workspace & 255) != 0 || workspace_bytes_given < need)
+        return PASA_ERR_WORKSPACE;
+    return PASA_OK;
+}
+
+// pasa_attn_decode: shapes and the split count (the workspace is checked
+// separately).
+inline int decode(const void* q, const void* k, const void* v, const void* o, int batch,
+                  int seqlen_kv, int num_heads_q, int gqa_group, int head_dim, float softmax_scale,
+                  int num_splits, int* n_used) {
+    const int rc = common(q, k, v, o, batch, 1, seqlen_kv, num_heads_q, gqa_group, head_dim,
+                          softmax_scale);
+    if (rc != PASA_OK) return rc;
+    return decode_split_count(batch, seqlen_kv, num_heads_q, gqa_group, head_dim, num_splits, n_used);
+}
+
+// pasa_attn_decode_paged: the paging arguments, then the checks of the
+// contiguous decode with page_size * max_pages_per_seq keys.
+inline int decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                        const int* block_table, const int* seq_lens, const void* o, int batch,
+                        int num_heads_q, int gqa_group, int head_dim, int page_size, int num_pages,
+                        int max_pages_per_seq, float softmax_scale, int num_splits, int* n_used) {
+    if (!block_table || !seq_lens) return PASA_ERR_INVALID;
+    if (page_size < 1 || num_pages < 1 || max_pages_per_seq < 1) return PASA_ERR_INVALID;
+    if (page_size % kDecodeBlock != 0) return PASA_ERR_UNSUPPORTED;
+    const int64_t max_keys = (int64_t)page_size * max_pages_per_seq;
+    if (max_keys > 0x7fffffff) return PASA_ERR_UNSUPPORTED;
+    const int seqlen_kv = (int)max_keys;
+    int rc = common(q, k_pages, v_pages, o, batch, 1, seqlen_kv, num_heads_q, gqa_group, head_dim,
+                    softmax_scale);
+    if (rc != PASA_OK) return rc;
+    if (!fits(num_pages, page_size, num_heads_q / gqa_group, head_dim)) return PASA_ERR_UNSUPPORTED;
+    if ((int64_t)batch * max_pages_per_seq > 0x7fffffff) return PASA_ERR_UNSUPPORTED;
+    return decode_split_count(batch, seqlen_kv, num_heads_q, gqa_group, head_dim, num_splits, n_used);
+}
+
+// pasa_attn_decode_combine.
+inline int combine(const float* o_part, const float* lse_part, const void* o, int batch,
+                   int num_heads_q, int head_dim, int num_splits) {
+    if (!o_part || !lse_part || !o) return PASA_ERR_INVALID;
+    if (batch < 1 || num_heads_q < 1 || head_dim < 1 || num_splits < 1) return PASA_ERR_INVALID;
+    if (!supported_dim(head_dim)) return PASA_ERR_UNSUPPORTED;
+    if ((int64_t)batch * num_heads_q > 0x7fffffff) return PASA_ERR_UNSUPPORTED;
+    return PASA_OK;
+}
+
+}  // namespace validate
+}  // namespace pasa

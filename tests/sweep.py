@@ -24,6 +24,8 @@ What a point reports
                    in binary64 on the sampled rows (the kernels take the same
                    decision in fp32, branch-free, and keep no count)
   <kernel>_nonfinite, <kernel>_rel_rmse   per kernel, on the sampled rows
+  <kernel>_head_max, <kernel>_row_max     worst per-head relative RMSE and
+                   worst per-row relative error over the sampled rows
 
 `python -m tests.sweep --replay-only [--full]` computes only the columns that
 need no GPU (scores, predicted overflow, refine rate).
@@ -36,7 +38,7 @@ import numpy as np
 
 import workloads as W
 from oracle import attn_fp64
-from workloads.metrics import nonfinite, rel_rmse
+from workloads.metrics import grouped_rel_rmse, nonfinite, rel_rmse, row_rel_err
 
 FP16_INF_EDGE = 65520.0          # smallest magnitude that rounds to fp16 infinity
 STRICT_RANGE = 3.2e4             # |c * score| below which the strict variant is specified
@@ -63,6 +65,11 @@ def points(full=False):
     for S in seqs:
         for amp in ((16, 32, 48, 64) if full else (16, 48)):
             pts.append(dict(kind="resonance", seq=S, D=64, causal=False, amp=float(amp)))
+        # resonance phase offset between query and key (the whole key range
+        # offset by the same angle): scores ~ 48^2 * 32 * cos(offset)
+        for eighths in ((0, 1, 2, 3, 4, 5, 6, 7, 8) if full else (0, 2, 4, 6, 8)):
+            pts.append(dict(kind="phase", seq=S, D=64, causal=False, amp=48.0,
+                            offset=eighths * math.pi / 8))
     return pts
 
 
@@ -76,6 +83,10 @@ def workload(pt, seed):
         a, b = pt["amp"], pt["bias"]
         return W.custom(1, S, S, heads, 1, D, pt["causal"], kind="amp_bias", seed=seed,
                         amp_lo=a, amp_hi=a, bias_lo=b, bias_hi=b)
+    if pt["kind"] == "phase":
+        return W.custom(1, S, S, heads, heads, D, pt["causal"], kind="resonance", seed=seed,
+                        amp=pt["amp"], period=64, flip_at=S, per_row_phase=False,
+                        phase_offset=pt["offset"])
     return W.custom(1, S, S, heads, heads, D, pt["causal"], kind="resonance", seed=seed,
                     amp=pt["amp"], period=64, flip_at=S // 2, per_row_phase=False)
 
@@ -174,6 +185,8 @@ def measure(pasa, pt, seed=0, n_rows=256):
     ro, _ = attn_fp64(q, k, v, w.scale, w.causal, rows=rows)
     tq, tk, tv = (torch.from_numpy(x).cuda() for x in (q, k, v))
     h, i = np.divmod(rows, w.seqlen_q)
+    vf = v.astype(np.float64)
+    floor = 0.25 * float(np.sqrt(np.mean(vf * vf) * vf.shape[-1]))
     res = dict(pt, heads=w.heads_q, max_abs_s=mx, s_rows="all" if all_rows else "sampled",
                naive_overflow=bool(mx >= FP16_INF_EDGE),
                max_abs_cs=mx * w.scale / math.log(2.0),
@@ -186,17 +199,24 @@ def measure(pasa, pt, seed=0, n_rows=256):
         bad = nonfinite(o)
         sel = o[0, i, h].astype(np.float64)
         res[f"{name}_nonfinite"] = int(bad)
-        res[f"{name}_rel_rmse"] = (rel_rmse(sel, ro) if np.all(np.isfinite(sel)) else float("nan"))
+        fin = bool(np.all(np.isfinite(sel)))
+        res[f"{name}_rel_rmse"] = rel_rmse(sel, ro) if fin else float("nan")
+        res[f"{name}_head_max"] = (max(grouped_rel_rmse(sel, ro, h).values()) if fin
+                                   else float("nan"))
+        res[f"{name}_row_max"] = (float(row_rel_err(sel, ro, floor).max()) if fin
+                                  else float("nan"))
     return res
 
 
 def onsets(results):
-    """Smallest bias (amplitude) at which the naive kernel produced inf/NaN, per
-    (kind, seq, D), beside the smallest one predicted from the scores."""
+    """Smallest bias (amplitude; |cos| of the phase offset) at which the naive
+    kernel produced inf/NaN, per (kind, seq, D), beside the smallest one
+    predicted from the scores."""
     out = {}
     for r in results:
         key = (r["kind"], r["seq"], r["D"])
-        x = r.get("bias") if r["kind"] == "bias" else r.get("amp")
+        x = (r.get("bias") if r["kind"] == "bias"
+             else abs(math.cos(r["offset"])) if r["kind"] == "phase" else r.get("amp"))
         o = out.setdefault(key, {"observed": None, "predicted": None})
         if r["naive_nonfinite"] and (o["observed"] is None or x < o["observed"]):
             o["observed"] = x

@@ -11,8 +11,8 @@ import pytest
 
 import workloads as W
 from oracle import attn_fp64
-from tests.gpu_common import (REL_RMSE_MAX, gather_rows, lse_error, lse_ok, nonfinite,
-                              rel_rmse, sample_rows, say)
+from tests.gpu_common import (check_o, gather_rows, lse_error, lse_ok, nonfinite, row_heads,
+                              sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def run(pasa, w, rows=None):
     torch.cuda.synchronize()
     o, lse = o.cpu().numpy(), lse.cpu().numpy()
     ro, rl = attn_fp64(qd, kd, v, w.scale, w.causal, rows=rows)
-    return o, lse, ro, rl
+    return o, lse, ro, rl, v
 
 
 @pytest.mark.parametrize("shape", [(1, 127, 300, 7, 1, 64, True), (2, 300, 129, 2, 2, 128, False),
@@ -55,11 +55,8 @@ def test_fp8_small_shapes_vs_oracle(pasa, shape):
     B, Sq, Skv, Hq, Hkv, D, causal = shape
     w = W.custom(B, Sq, Skv, Hq, Hkv, D, causal, kind="bias", seed=sum(shape), bias=3.0)
     say("fp8 case", shape)
-    o, lse, ro, rl = run(pasa, w)
-    assert nonfinite(o) == 0
-    err = rel_rmse(o, ro)
-    say("rel_rmse", err)
-    assert err <= REL_RMSE_MAX
+    o, lse, ro, rl, v = run(pasa, w)
+    check_o(o, ro, v, label=f"fp8 {shape}")
     assert lse_ok(lse, rl, rel_tol=LSE_REL)
 
 
@@ -68,10 +65,9 @@ def test_fp8_configs_vs_oracle(pasa, name):
     w = W.CONFIGS[name]
     say("fp8 config", name)
     rows = None if name == "c1" else sample_rows(w, 512, np.random.default_rng(8))
-    o, lse, ro, rl = run(pasa, w, rows)
+    o, lse, ro, rl, v = run(pasa, w, rows)
     assert nonfinite(o) == 0 and nonfinite(lse) == 0
     go, gl = (o, lse) if rows is None else gather_rows(o, lse, w, rows)
-    err = rel_rmse(go, ro)
-    say(name, "fp8 rel_rmse", err, "lse_err", lse_error(gl, rl))
-    assert err <= REL_RMSE_MAX
+    check_o(go, ro, v, heads=None if rows is None else row_heads(w, rows), label=f"fp8 {name}")
+    say(name, "fp8 lse_err", lse_error(gl, rl))
     assert lse_ok(gl, rl, rel_tol=LSE_REL)

@@ -33,9 +33,22 @@ def test_bench_traffic_guard_tracks_sources():
     import bench
     h = bench.source_hash()
     assert len(h) == 64
-    p, d = bench.recorded_traffic()
-    text = open(bench.TRAFFIC_FILE).read() if os.path.exists(bench.TRAFFIC_FILE) else ""
+    p, d = bench.recorded_traffic("qwen2")
+    f = bench.traffic_file("qwen2")
+    text = open(f).read() if os.path.exists(f) else ""
     if f"source_sha256={h}" in text:
         assert p is not None and d is not None
     else:
         assert p is None and d is None
+
+
+def test_profile_commands_run_committed_files_only():
+    """Every rocprofv3 command a profile summary records runs bench.py, which
+    is committed, and never a working file."""
+    sys.path.insert(0, ROOT)
+    import bench
+    for set_name in bench.PROFILE_SETS:
+        for kind in ("trace", "pmc1", "pmc2", "fetch", "write", "cfetch", "cwrite"):
+            cmd = bench.profile_cmd(set_name, kind)
+            assert cmd.startswith("rocprofv3 ") and "-- python bench.py" in cmd
+            assert "_work" not in cmd

@@ -6,7 +6,7 @@ import pytest
 
 import workloads as W
 from oracle import attn_fp64
-from tests.gpu_common import REL_RMSE_MAX, lse_ok, nonfinite, rel_rmse, say
+from tests.gpu_common import REL_RMSE_MAX, check_o, lse_ok, nonfinite, rel_rmse, say
 
 pytestmark = pytest.mark.gpu
 
@@ -89,9 +89,7 @@ def test_paged_decode_vs_oracle(pasa, case):
         if n == 0:
             assert np.all(o[b] == 0) and np.all(np.isneginf(lse[b]))
     nz = [b for b, n in enumerate(lens) if n > 0]
-    err = rel_rmse(o[nz], ro[nz])
-    say("rel_rmse", err)
-    assert err <= REL_RMSE_MAX
+    check_o(o[nz], ro[nz], vp, label=f"paged {case}")
     assert lse_ok(lse, rl)
 
 
@@ -131,8 +129,7 @@ def test_paged_out_of_range_page_reads_zero(pasa):
     ref_table = table.copy()
     ref_table[0, 1] = kz.shape[0] - 1
     ro, rl = oracle_paged(q, kz, vz, ref_table, ln, scale)
-    assert nonfinite(o) == 0
-    assert rel_rmse(o, ro) <= REL_RMSE_MAX
+    check_o(o, ro, vp, label="paged out-of-range page")
     assert lse_ok(lse, rl)
 
 
@@ -167,8 +164,5 @@ def test_paged_single_split_over_shuffled_pool_vs_oracle(pasa):
     q, kp, vp, table, ln = paged_case(len(lens), lens, Hq, Hkv, D, ps, seed=13)
     o, lse, scale = run_paged(pasa, q, kp, vp, table, ln, num_splits=1)
     ro, rl = oracle_paged(q, kp, vp, table, ln, scale)
-    assert nonfinite(o) == 0
-    err = rel_rmse(o, ro)
-    say("rel_rmse", err)
-    assert err <= REL_RMSE_MAX
+    check_o(o, ro, vp, label="paged single split")
     assert lse_ok(lse, rl)

@@ -1,14 +1,16 @@
 """GPU parity: the HIP path against the binary64 oracle on identical seeded
-fp16 inputs.  The bar is relative RMSE of O <= 2e-3 and no inf/NaN; lse within
-1e-2 absolute (or 1e-6 relative above 1e4).  The naive fp16 kernel's overflow
-on the large-bias and resonance inputs is recorded alongside."""
+fp16 inputs.  The bar is relative RMSE of O <= 2e-3 over the output and over
+every (batch, head), the worst row within 1e-2 (tests/gpu_common.py explains
+the row measure), no inf/NaN; lse within 1e-2 absolute (or 1e-6 relative above
+1e4).  The naive fp16 kernel's overflow on the large-bias and resonance inputs
+is recorded alongside."""
 import numpy as np
 import pytest
 
 import workloads as W
 from oracle import attn_fp64, combine_fp64
-from tests.gpu_common import (REL_RMSE_MAX, gather_rows, lse_error, lse_ok, nonfinite, rel_rmse,
-                              sample_rows, say, to_gpu)
+from tests.gpu_common import (REL_RMSE_MAX, check_o, gather_rows, head_rows, lse_error, lse_ok,
+                              nonfinite, rel_rmse, row_heads, sample_rows, say, to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -44,15 +46,12 @@ def test_small_shapes_vs_oracle(pasa, shape):
     say("case", shape)
     (q, k, v), o, lse = run_fwd(pasa, w)
     ro, rl = attn_fp64(q, k, v, w.scale, causal)
-    assert nonfinite(o) == 0
     # rows with no visible key (causal, Sq > Skv) are exactly zero
     empty = np.isneginf(rl)
     if empty.any():
         b, h, i = np.nonzero(empty)
         assert np.all(o[b, i, h] == 0)
-    err = rel_rmse(o, ro)
-    say("rel_rmse", err)
-    assert err <= REL_RMSE_MAX
+    check_o(o, ro, v, label=str(shape))
     assert lse_ok(lse, rl)
 
 
@@ -62,11 +61,9 @@ def test_config_full_vs_oracle(pasa, name):
     say("config", name)
     (q, k, v), o, lse = run_fwd(pasa, w)
     ro, rl = attn_fp64(q, k, v, w.scale, w.causal)
-    n_bad = nonfinite(o) + nonfinite(lse)
-    err = rel_rmse(o, ro)
-    say(name, "rel_rmse", err, "nonfinite", n_bad, "lse_err", lse_error(lse, rl)[:2])
-    assert n_bad == 0
-    assert err <= REL_RMSE_MAX
+    assert nonfinite(lse) == 0
+    check_o(o, ro, v, label=name)
+    say(name, "lse_err", lse_error(lse, rl)[:2])
     assert lse_ok(lse, rl)
 
 
@@ -78,11 +75,9 @@ def test_strict_config_full_vs_oracle(pasa, name):
     say("strict config", name)
     (q, k, v), o, lse = run_fwd(pasa, w, strict=True)
     ro, rl = attn_fp64(q, k, v, w.scale, w.causal)
-    n_bad = nonfinite(o) + nonfinite(lse)
-    err = rel_rmse(o, ro)
-    say(name, "strict rel_rmse", err, "nonfinite", n_bad, "lse_err", lse_error(lse, rl)[:2])
-    assert n_bad == 0
-    assert err <= REL_RMSE_MAX
+    assert nonfinite(lse) == 0
+    check_o(o, ro, v, label="strict " + name)
+    say(name, "strict lse_err", lse_error(lse, rl)[:2])
     assert lse_ok(lse, rl)
 
 
@@ -94,10 +89,7 @@ def test_strict_small_shapes_vs_oracle(pasa, shape):
     say("strict case", shape)
     (q, k, v), o, lse = run_fwd(pasa, w, strict=True)
     ro, rl = attn_fp64(q, k, v, w.scale, causal)
-    assert nonfinite(o) == 0
-    err = rel_rmse(o, ro)
-    say("rel_rmse", err)
-    assert err <= REL_RMSE_MAX
+    check_o(o, ro, v, label="strict " + str(shape))
     assert lse_ok(lse, rl)
 
 
@@ -112,24 +104,98 @@ def test_chunked_prefill_against_cache_vs_oracle(pasa, Sq, Skv):
     ro, rl = attn_fp64(q, k, v, w.scale, True, rows=rows)
     go, gl = gather_rows(o, lse, w, rows)
     assert nonfinite(o) == 0
-    err = rel_rmse(go, ro)
-    say("rel_rmse", err)
-    assert err <= REL_RMSE_MAX
+    check_o(go, ro, v, heads=row_heads(w, rows), label=f"chunked {Sq}x{Skv}")
     assert lse_ok(gl, rl)
 
 
-def test_c4_sampled_rows_vs_oracle(pasa):
+@pytest.fixture(scope="module")
+def c4_run(pasa):
+    """The long-context workload through PASA and the naive kernel, once."""
+    import torch
     w = W.CONFIGS["c4"]
-    say("config c4 (sampled rows)")
-    (q, k, v), o, lse = run_fwd(pasa, w)
+    say("config c4: generating inputs")
+    q, k, v = W.generate(w)
+    tq, tk, tv = to_gpu(q, k, v)
+    o, lse = pasa.attn_fwd(tq, tk, tv, causal=True, scale=w.scale)
+    on, _ = pasa.naive_attn_fwd(tq, tk, tv, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    res = dict(w=w, q=q, k=k, v=v, o=o.cpu().numpy(), lse=lse.cpu().numpy(), naive=on.cpu().numpy())
+    del tq, tk, tv, o, lse, on
+    torch.cuda.empty_cache()
+    return res
+
+
+def c4_extreme_heads(w, n=4):
+    """Query heads with the largest amplitude product a_q*a_k and the largest
+    bias product b_q*b_k (n of each): the heads most exposed to the overflow
+    mechanisms the PASA page names."""
+    aq, bq, ak, bk = W.head_params(w)
+    kv = np.arange(w.heads_q) // w.group
+    amp, bias = aq * ak[kv], bq * bk[kv]
+    return sorted(set(np.argsort(-amp)[:n].tolist()) | set(np.argsort(-bias)[:n].tolist()))
+
+
+def test_c4_extreme_heads_and_one_percent_vs_oracle(c4_run):
+    """All rows of the most exposed heads, 1 % of the rows of every other head."""
+    w, q, k, v, o, lse = (c4_run[x] for x in ("w", "q", "k", "v", "o", "lse"))
     assert nonfinite(o) == 0 and nonfinite(lse) == 0
-    rows = sample_rows(w, 384, np.random.default_rng(44))
+    heads = c4_extreme_heads(w)
+    say("c4 full heads", heads)
+    rows = head_rows(w, set(heads), 0.01, np.random.default_rng(44))
     ro, rl = attn_fp64(q, k, v, w.scale, w.causal, rows=rows)
     go, gl = gather_rows(o, lse, w, rows)
-    err = rel_rmse(go, ro)
-    say("c4 sampled rel_rmse", err)
-    assert err <= REL_RMSE_MAX
+    check_o(go, ro, v, heads=row_heads(w, rows), label="c4")
+    full = np.isin(row_heads(w, rows), heads)
+    for h in heads:
+        sel = row_heads(w, rows) == h
+        say("c4 head", h, "rel_rmse", rel_rmse(go[sel], ro[sel]))
+    say("c4 rows compared", rows.size, "of which in full heads", int(full.sum()))
     assert lse_ok(gl, rl)
+
+
+def c4_head_bounds(w, q, k):
+    """Per query head: an upper bound on max |q.k| (Cauchy-Schwarz over the
+    largest row norms) and a lower bound (the largest |q.k| over a sample of
+    query rows against every key)."""
+    kmax = [float(np.sqrt(np.sum(k[0, :, j].astype(np.float64) ** 2, axis=-1)).max())
+            for j in range(w.heads_kv)]
+    rng = np.random.default_rng(45)
+    upper, lower = [], []
+    for h in range(w.heads_q):
+        kvh = h // w.group
+        qmax = float(np.sqrt(np.sum(q[0, :, h].astype(np.float64) ** 2, axis=-1)).max())
+        upper.append(qmax * kmax[kvh])
+        ii = rng.choice(w.seqlen_q, 16, replace=False)
+        s = q[0, ii, h].astype(np.float64) @ k[0, :, kvh].astype(np.float64).T
+        s = np.where(np.arange(w.seqlen_kv)[None, :] <= ii[:, None], s, 0.0)
+        lower.append(float(np.abs(s).max()))
+    return np.array(upper), np.array(lower)
+
+
+def test_c4_naive_overflows_on_the_exposed_heads(c4_run):
+    """The naive fp16 kernel: heads with some unscaled |q.k| above the fp16
+    range produce inf/NaN, heads whose every |q.k| provably stays below it do
+    not, and the finite heads' error is reported."""
+    w, q, k, v, on = (c4_run[x] for x in ("w", "q", "k", "v", "naive"))
+    upper, lower = c4_head_bounds(w, q, k)
+    bad = np.array([nonfinite(on[0, :, h]) for h in range(w.heads_q)])
+    say("c4 naive non-finite per head", bad.tolist())
+    say("c4 naive heads with inf/NaN", int(np.count_nonzero(bad)), "of", w.heads_q,
+        "outputs", int(bad.sum()), "of", on.size)
+    assert bad.sum() > 0
+    for h in range(w.heads_q):
+        if lower[h] > 66000.0:
+            assert bad[h] > 0, (h, lower[h])
+        if upper[h] < 65000.0:
+            assert bad[h] == 0, (h, upper[h])
+    fin = [h for h in range(w.heads_q) if bad[h] == 0]
+    if fin:
+        rng = np.random.default_rng(46)
+        rows = np.concatenate([h * w.seqlen_q + np.sort(rng.choice(w.seqlen_q, 64, replace=False))
+                               for h in fin])
+        ro, _ = attn_fp64(q, k, v, w.scale, True, rows=rows)
+        go = on[0, rows % w.seqlen_q, rows // w.seqlen_q]
+        say("c4 naive rel_rmse on its finite heads (sampled rows)", rel_rmse(go, ro))
 
 
 def test_stress_jump_above_fp16_range(pasa):
@@ -137,10 +203,7 @@ def test_stress_jump_above_fp16_range(pasa):
     w = W.custom(1, 512, 512, 4, 1, 128, True, kind="jump", seed=77, jump_at=200)
     (q, k, v), o, lse = run_fwd(pasa, w)
     ro, rl = attn_fp64(q, k, v, w.scale, True)
-    assert nonfinite(o) == 0
-    err = rel_rmse(o, ro)
-    say("jump rel_rmse", err)
-    assert err <= REL_RMSE_MAX
+    check_o(o, ro, v, label="jump")
     assert lse_ok(lse, rl)
 
 
@@ -149,10 +212,7 @@ def test_resonance_per_row_phase_stress(pasa):
                  period=64, flip_at=512, per_row_phase=True)
     (q, k, v), o, lse = run_fwd(pasa, w)
     ro, rl = attn_fp64(q, k, v, w.scale, False)
-    assert nonfinite(o) == 0
-    err = rel_rmse(o, ro)
-    say("per-row-phase resonance rel_rmse", err)
-    assert err <= REL_RMSE_MAX
+    check_o(o, ro, v, label="per-row-phase resonance")
 
 
 def test_deterministic(pasa):
@@ -179,8 +239,10 @@ def test_naive_overflows_where_pasa_does_not(pasa, name):
     w = W.CONFIGS[name]
     (_, _, _), o, _ = run_fwd(pasa, w, naive=True)
     bad = nonfinite(o)
-    say(name, "naive non-finite outputs:", bad, "of", o.size)
-    assert bad > 0
+    per_head = [nonfinite(o[:, :, h]) for h in range(w.heads_q)]
+    say(name, "naive non-finite outputs:", bad, "of", o.size, "per head", per_head)
+    # every head of these inputs has unscaled scores beyond the fp16 range
+    assert all(x > 0 for x in per_head)
 
 
 # ----------------------------------------------------------------- decode
@@ -194,10 +256,8 @@ def test_c5_decode_vs_oracle(pasa):
     torch.cuda.synchronize()
     o, lse = o.cpu().numpy(), lse.cpu().numpy()
     ro, rl = attn_fp64(q, k, v, w.scale, False)
-    err = rel_rmse(o, ro)
-    say("c5 rel_rmse", err, "nonfinite", nonfinite(o))
-    assert nonfinite(o) == 0 and nonfinite(lse) == 0
-    assert err <= REL_RMSE_MAX
+    assert nonfinite(lse) == 0
+    check_o(o, ro, v, label="c5 decode")
     assert lse_ok(lse, rl[:, :, 0])
 
 
@@ -213,9 +273,7 @@ def test_decode_shapes_vs_oracle(pasa, Skv, n, Hq, Hkv, D):
     o, lse = pasa.attn_decode(tq, tk, tv, num_splits=n, scale=w.scale)
     torch.cuda.synchronize()
     ro, rl = attn_fp64(q, k, v, w.scale, False)
-    err = rel_rmse(o.cpu().numpy(), ro)
-    say("decode", (Skv, n, Hq, Hkv, D), "rel_rmse", err)
-    assert err <= REL_RMSE_MAX
+    check_o(o.cpu().numpy(), ro, v, label=f"decode {(Skv, n, Hq, Hkv, D)}")
     assert lse_ok(lse.cpu().numpy(), rl[:, :, 0])
 
 
@@ -244,9 +302,7 @@ def test_decode_combine_entry_on_oracle_partials(pasa):
     tpl = torch.from_numpy(pl.astype(np.float32)).cuda()
     o, lse = pasa.attn_decode_combine(tpo, tpl)
     torch.cuda.synchronize()
-    err = rel_rmse(o.cpu().numpy(), ro)
-    say("combine rel_rmse", err)
-    assert err <= 1e-3
+    check_o(o.cpu().numpy(), ro, v, label="combine", rel_max=1e-3)
     assert lse_ok(lse.cpu().numpy(), rl[:, :, 0], abs_tol=1e-4)
 
 
@@ -286,6 +342,19 @@ def test_binding_rejects_wrong_output_buffers(pasa):
     qp = torch.zeros((1, 8, 2, 64), dtype=torch.float16, device="cuda")
     with pytest.raises(ValueError):
         pasa.attn_fwd(qp, qp, qp, out=torch.empty((1, 8, 2, 32), dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError):
+        pasa.attn_fwd(qp, qp, qp, lse=torch.empty((1, 2, 7), dtype=torch.float32, device="cuda"))
+    # the e4m3 entry point: wrong dtype, wrong shape, host tensor
+    q8 = qp.to(torch.float8_e4m3fn)
+    for bad in (torch.empty((1, 8, 2, 64), dtype=torch.float32, device="cuda"),
+                torch.empty((1, 8, 2, 32), dtype=torch.float16, device="cuda"),
+                torch.empty((1, 8, 2, 64), dtype=torch.float16)):
+        with pytest.raises(ValueError):
+            pasa.attn_fwd_fp8(q8, q8, qp, 1.0, 1.0, out=bad)
+    for bad in (torch.empty((1, 2, 8), dtype=torch.float16, device="cuda"),
+                torch.empty((1, 2, 9), dtype=torch.float32, device="cuda")):
+        with pytest.raises(ValueError):
+            pasa.attn_fwd_fp8(q8, q8, qp, 1.0, 1.0, lse=bad)
     torch.cuda.synchronize()
 
 
@@ -304,11 +373,7 @@ def test_max_kv_length_flat_rows(pasa, causal):
     o, lse = pasa.attn_fwd(tq, tk, tv, causal=causal, scale=w.scale)
     torch.cuda.synchronize()
     ro, rl = attn_fp64(q, k, v, w.scale, causal)
-    o = o.cpu().numpy()
-    err = rel_rmse(o, ro)
-    say("flat 65504 rel_rmse", err)
-    assert nonfinite(o) == 0
-    assert err <= REL_RMSE_MAX
+    check_o(o.cpu().numpy(), ro, v, label="flat 65504")
     assert lse_ok(lse.cpu().numpy(), rl)
 
 
@@ -342,9 +407,7 @@ def test_noncausal_full_round_vs_oracle(pasa, D):
     ro, rl = attn_fp64(q, k, v, w.scale, False, rows=rows)
     go, gl = gather_rows(o, lse, w, rows)
     assert nonfinite(o) == 0
-    err = rel_rmse(go, ro)
-    say("rel_rmse", err)
-    assert err <= REL_RMSE_MAX
+    check_o(go, ro, v, heads=row_heads(w, rows), label=f"one round D{D}")
     assert lse_ok(gl, rl)
 
 

@@ -3,9 +3,11 @@ bar everywhere, the strict variant within the bar inside its stated range, and
 the naive fp16 kernel overflowing exactly where an unscaled score rounds to
 fp16 infinity ("Online Pseudo-average Shifting Attention (PASA) ...",
 Abstract: overflow above 65504)."""
+import math
+
 import pytest
 
-from tests.gpu_common import REL_RMSE_MAX, say
+from tests.gpu_common import REL_RMSE_MAX, ROW_REL_MAX, say
 from tests.sweep import STRICT_RANGE, measure, onsets, points
 
 pytestmark = pytest.mark.gpu
@@ -33,6 +35,20 @@ def test_pasa_within_bar_everywhere(results):
     for r in results:
         assert r["pasa_nonfinite"] == 0, r
         assert r["pasa_rel_rmse"] <= REL_RMSE_MAX, r
+        assert r["pasa_head_max"] <= REL_RMSE_MAX, r
+        assert r["pasa_row_max"] <= ROW_REL_MAX, r
+
+
+def test_grid_spans_phase_offsets(results):
+    """At least three query/key phase offsets, with the naive overflow on the
+    in-phase and anti-phase ends and none at a quarter turn."""
+    ph = [r for r in results if r["kind"] == "phase"]
+    assert len({round(r["offset"], 6) for r in ph}) >= 3
+    for r in ph:
+        if abs(math.cos(r["offset"])) < 0.75:
+            assert not r["naive_overflow"] and r["naive_nonfinite"] == 0, r
+        if abs(math.cos(r["offset"])) > 0.99:
+            assert r["naive_overflow"] and r["naive_nonfinite"] > 0, r
 
 
 def test_strict_within_bar_inside_its_range(results):
@@ -41,6 +57,7 @@ def test_strict_within_bar_inside_its_range(results):
     for r in inside:
         assert r["strict_nonfinite"] == 0, r
         assert r["strict_rel_rmse"] <= REL_RMSE_MAX, r
+        assert r["strict_head_max"] <= REL_RMSE_MAX, r
 
 
 def test_naive_overflows_exactly_where_predicted(results):

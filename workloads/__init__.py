@@ -124,6 +124,25 @@ def _normal_fp16(rng, shape, mul=None, add=None, chunk_axis0=True):
     return out
 
 
+def _amp_bias_params(rp, w):
+    """Per-head amplitude and bias draws of the "amp_bias" recipe, in the order
+    they are taken from the parameter stream: a_q, b_q (one per query head),
+    a_k, b_k (one per key/value head)."""
+    p = w.params
+    aq = rp.uniform(p.get("amp_lo", 0.5), p.get("amp_hi", 4.0), w.heads_q)
+    bq = rp.uniform(p.get("bias_lo", 0.0), p.get("bias_hi", 30.0), w.heads_q)
+    ak = rp.uniform(p.get("amp_lo", 0.5), p.get("amp_hi", 4.0), w.heads_kv)
+    bk = rp.uniform(p.get("bias_lo", 0.0), p.get("bias_hi", 30.0), w.heads_kv)
+    return aq, bq, ak, bk
+
+
+def head_params(w: Workload):
+    """(a_q, b_q, a_k, b_k) of an "amp_bias" workload, as generate() draws them."""
+    if w.kind != "amp_bias":
+        raise ValueError("head_params: only the amp_bias recipe has per-head draws")
+    return _amp_bias_params(_streams(w.seed)[3], w)
+
+
 def generate(w: Workload):
     """Return (q, k, v) as contiguous fp16 numpy arrays in BSHD layout."""
     rq, rk, rv, rp = _streams(w.seed)
@@ -139,10 +158,7 @@ def generate(w: Workload):
         q = _normal_fp16(rq, qs, add=bias)
         k = _normal_fp16(rk, ks, add=bias)
     elif w.kind == "amp_bias":
-        aq = rp.uniform(p.get("amp_lo", 0.5), p.get("amp_hi", 4.0), Hq)
-        bq = rp.uniform(p.get("bias_lo", 0.0), p.get("bias_hi", 30.0), Hq)
-        ak = rp.uniform(p.get("amp_lo", 0.5), p.get("amp_hi", 4.0), Hkv)
-        bk = rp.uniform(p.get("bias_lo", 0.0), p.get("bias_hi", 30.0), Hkv)
+        aq, bq, ak, bk = _amp_bias_params(rp, w)
         q = _normal_fp16(rq, qs, mul=aq[:, None], add=bq[:, None])
         k = _normal_fp16(rk, ks, mul=ak[:, None], add=bk[:, None])
     elif w.kind == "resonance":
@@ -160,7 +176,10 @@ def generate(w: Workload):
             phi = rp.uniform(0.0, 2.0 * math.pi, (B, Hq))
             phi_q = np.broadcast_to(phi[:, None, :], (B, Sq, Hq))
             phi_k = np.broadcast_to(phi[:, None, :], (B, Skv, Hkv)).copy()
-        phi_k = phi_k + math.pi * (np.arange(Skv) >= flip_at)[None, :, None]
+        # key phase = query phase + phase_offset, plus pi from row flip_at on
+        # (flip_at = Skv: no flip)
+        phi_k = (phi_k + p.get("phase_offset", 0.0)
+                 + math.pi * (np.arange(Skv) >= flip_at)[None, :, None])
         q = np.empty(qs, np.float16)
         k = np.empty(ks, np.float16)
         for b in range(B):

@@ -31,10 +31,10 @@
  *  - On any error nothing is enqueued and no output byte is written.
  *  - Supported: head_dim 64 or 128; num_heads_q % gqa_group == 0; any
  *    batch >= 1 and sequence lengths from 1 to 2^31 - 512 (ragged tails are
- *    masked), within the per-call limits each entry point lists.
- *    seqlen_kv <= 65504 for pasa_attn_fwd and pasa_naive_attn_fwd, because the
- *    running softmax sum is carried in fp16; the split-KV decode path has no
- *    such bound (each split's sum is at most 65504 keys; the combine is fp32).
+ *    masked), within the per-call limits each entry point lists.  The running
+ *    softmax sum is an fp16 (hi, lo) pair over each segment of 32768 keys, and
+ *    the completed segments' sums are carried in fp32, so the key count has no
+ *    fp16 bound.
  */
 #ifndef PASA_ATTN_H
 #define PASA_ATTN_H
@@ -62,11 +62,13 @@ typedef enum {
  *   lse       device fp32 [B,Hq,Sq], written; may be NULL (not computed).
  *   softmax_scale  multiplies q.k before the softmax (e.g. 1/sqrt(head_dim)).
  *   causal    0 or 1 (bottom-right aligned).
- * Errors: PASA_ERR_INVALID for a null q/k/v/o, a size < 1, or
- * num_heads_q % gqa_group != 0; PASA_ERR_UNSUPPORTED for head_dim not in
- * {64,128}, seqlen_kv > 65504, a non-finite or non-positive softmax_scale,
- * sizes whose element count overflows 64-bit indexing, or more than 2^31 - 1
- * work items of 256 query rows of one head (batch * num_heads_q *
+ * Errors: PASA_ERR_INVALID for a null q/k/v/o, a size < 1, a causal flag
+ * other than 0 or 1, or num_heads_q % gqa_group != 0; PASA_ERR_UNSUPPORTED
+ * for head_dim not in {64,128}, a sequence length above 2^31 - 512, a
+ * non-finite or non-positive softmax_scale, sizes whose element count
+ * overflows 64-bit indexing, one head's K or V slab of one sequence above
+ * 4 GiB (seqlen_kv * (num_heads_q / gqa_group) * head_dim * 2 bytes), or more
+ * than 2^31 - 1 work items of 256 query rows of one head (batch * num_heads_q *
  * ceil(seqlen_q / 256)).
  */
 int pasa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -150,10 +152,10 @@ int pasa_naive_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
  *               lse_part [batch, num_heads_q, n].  Its contents on return are
  *               the partials of this call.
  * Launches the split kernel and the combine kernel on `stream`, in order.
- * Errors: the argument checks of pasa_attn_fwd (without the seqlen_kv bound
- * and the prefill work-item limit), plus PASA_ERR_WORKSPACE for a null,
+ * Errors: the argument checks of pasa_attn_fwd (without the prefill
+ * work-item limit), plus PASA_ERR_WORKSPACE for a null,
  * misaligned or too-small workspace, PASA_ERR_INVALID for num_splits < 0, and
- * PASA_ERR_UNSUPPORTED when a split would sum more than 65504 keys, for more
+ * PASA_ERR_UNSUPPORTED for more
  * than 65535 splits, or when the split grid (batch * kv heads *
  * ceil(gqa_group / 32) * splits waves) or the combine grid (batch *
  * num_heads_q workgroups) exceeds 2^31 - 1.  More splits than 32-key

@@ -160,6 +160,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
         }
         const _Float16* Ks = slot_k(j);
         const _Float16* Vs = Ks + sub_halves<D>();
+        // every kSegKeys keys the fp16 running sum moves into the fp32 carry
+        if (j > 0 && j % (kSegKeys / kSub) == 0) fold_segment(st);
         f16v S[1];
         S[0] = qk_subtile_sw<D>(Ks, 0, qreg, n, hh);
         const int wbase = kbeg + j * kSub;
@@ -176,6 +178,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
             const float af = (float)alpha;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) acc[dt] *= af;
+            st.lc *= af;
         }
         pv_chunks_tr<D, 2>(Vs, 0, P, acc, lane);
     }

@@ -288,6 +288,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // arguments; the accumulator rescale the new running maximum calls for
     auto vphase = [&](int j) {
         if (!active(j)) return;
+        // every kSegKeys keys the fp16 running sum (complete up to block j-1,
+        // whose sum the matrix phase just added) moves into the fp32 carry
+        if (!NAIVE && j > 0 && j % (kSegKeys / kBC) == 0) fold_segment(st);
         const int kbase = (blk0 + j) * kBC;
         _Float16 d;
         if (kbase + kBC <= wave_lim_lo) {   // the whole block is visible to the wave
@@ -305,6 +308,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             const float af = (float)apend;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) acc[dt] *= af;
+            st.lc *= af;
         }
     };
 

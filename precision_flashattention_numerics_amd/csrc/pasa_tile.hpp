@@ -20,12 +20,15 @@
 //   P     = exp2(X);  r = sum_j P                                     (fp16)
 //   alpha = exp2(fp16(R - R'))                                        (fp16)
 //   (l_hi, l_lo) <- compensated fp16 sum of alpha*(l_hi, l_lo) + r    (fp16)
+//   every 32768 keys: l_c <- l_c + (l_hi + l_lo), (l_hi, l_lo) <- 0;
+//   l_c <- alpha*l_c on every block                                    (fp32)
 // where c = scale * log2(e).  X is the shifted tile fp16(c*S - off) moved
 // down by s, formed in a single rounding (s is known before the tile is
 // formed).  Because X is taken against off + s, P = exp2(c*S - R') up to
 // rounding whatever off was: the shift changes only which fp16 numbers are
-// formed, never the softmax (a per-row shift leaves softmax unchanged).  The epilogue recovers the exact log-sum-exp as
-// ln2 * (R + log2(l_hi + l_lo)).
+// formed, never the softmax (a per-row shift leaves softmax unchanged).  The
+// epilogue recovers the exact log-sum-exp as ln2 * (R + log2(L)) with
+// L = l_c + l_hi + l_lo.
 //
 // The naive variant rounds the UNSCALED S to fp16, scales it in fp16 and
 // keeps a plain running maximum: a half-precision Flash Attention without the
@@ -69,7 +72,25 @@ struct RowState {
     float R = -__builtin_inff();   // running maximum of c*S (log2 units)
     _Float16 lhi = 0, llo = 0;     // running sum (PASA): compensated fp16 pair
     float lsum = 0.0f;             // running sum (naive): fp32
+    float lc = 0.0f;               // PASA: the running sums of completed key segments
 };
+
+// Keys per segment of the PASA running sum.  The compensated fp16 pair sums at
+// most this many exponentials (each at most 1 up to rounding, since every
+// block is taken against its running maximum), then is folded into the fp32
+// carry `lc`: partial sums over disjoint key ranges taken against one running
+// maximum add ("Block Sparse Flash Attention" topic page, FoldAttention card:
+// normalised partials over disjoint key ranges compose), so no sequence length
+// can push the fp16 pair past 65504.  Each block's sum stays an fp16 sum.
+constexpr int kSegKeys = 32768;
+
+// Fold the compensated fp16 sum into the carry (at a segment boundary, when
+// both hold sums against the same running maximum).
+__device__ __forceinline__ void fold_segment(RowState& st) {
+    st.lc += (float)st.lhi + (float)st.llo;
+    st.lhi = 0;
+    st.llo = 0;
+}
 
 // One key block of NT 32-key sub-tiles for the row held by this lane (and by
 // the lane 32 apart, which holds the other half of the row's keys), in two
@@ -245,7 +266,7 @@ __device__ __forceinline__ _Float16 softmax_block(const f16v (&S)[NT], h2 (&P)[8
 
 template <bool NAIVE>
 __device__ __forceinline__ float row_sum(const RowState& st) {
-    return NAIVE ? st.lsum : (float)st.lhi + (float)st.llo;
+    return NAIVE ? st.lsum : st.lc + ((float)st.lhi + (float)st.llo);
 }
 
 // ---------------------------------------------------------------------------

@@ -14,7 +14,6 @@ namespace pasa {
 namespace validate {
 
 constexpr int kDecodeBlock = 32;         // keys per decode sub-tile; splits are whole sub-tiles
-constexpr int kMaxFp16Sum = 65504;       // keys one fp16 running sum may hold
 constexpr int kFwdRows = 256;            // query rows per prefill work item (at most)
 // Longest sequence: the kernels index rows as int, and a work item's last row
 // (its first row + 255) must not overflow.
@@ -60,7 +59,6 @@ inline int fwd(const void* q, const void* k, const void* v, const void* o, int b
                           softmax_scale);
     if (rc != PASA_OK) return rc;
     if (causal != 0 && causal != 1) return PASA_ERR_INVALID;
-    if (seqlen_kv > kMaxFp16Sum) return PASA_ERR_UNSUPPORTED;
     // the prefill's work items (up to 256 query rows of one head) are counted in int
     if ((int64_t)batch * num_heads_q * (((int64_t)seqlen_q + kFwdRows - 1) / kFwdRows) >
         0x7FFFFFFFLL)
@@ -119,9 +117,6 @@ inline int decode_split_count(int batch, int seqlen_kv, int num_heads_q, int gqa
     if (n > blocks) n = blocks;
     if (n < 1 || n > 65535 || !decode_grids_fit(batch, num_heads_q, gqa_group, n))
         return PASA_ERR_UNSUPPORTED;
-    // every split sums at most 65504 keys in fp16
-    const int64_t per_split = ((int64_t)blocks + n - 1) / n * kDecodeBlock;
-    if (per_split > kMaxFp16Sum) return PASA_ERR_UNSUPPORTED;
     *n_used = n;
     return PASA_OK;
 }

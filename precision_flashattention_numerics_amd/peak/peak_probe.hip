@@ -37,21 +37,26 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(float* out, int iters) {
     out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
-// Streaming read of n16 16-byte words, four independent non-temporal loads
-// in flight per lane per step, folded by xor so every byte is used.
+// Streaming read of n16 16-byte words: each workgroup reads one contiguous
+// chunk of the buffer, U independent non-temporal 16-byte loads per lane in
+// flight per step (consecutive lanes read consecutive words), folded by xor
+// so every byte is used.
+template <int U>
 __global__ __launch_bounds__(256) void hbm_read_kernel(const u4* __restrict__ src, int64_t n16,
                                                        uint32_t* out) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+    const int64_t beg = (int64_t)blockIdx.x * per;
+    const int64_t end = beg + per < n16 ? beg + per : n16;
+    int64_t i = beg + threadIdx.x;
     u4 acc = {0u, 0u, 0u, 0u};
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const u4 x0 = __builtin_nontemporal_load(src + i);
-        const u4 x1 = __builtin_nontemporal_load(src + i + stride);
-        const u4 x2 = __builtin_nontemporal_load(src + i + 2 * stride);
-        const u4 x3 = __builtin_nontemporal_load(src + i + 3 * stride);
-        acc ^= x0 ^ x1 ^ x2 ^ x3;
+    for (; i + (U - 1) * 256 < end; i += U * 256) {
+        u4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = __builtin_nontemporal_load(src + i + u * 256);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= x[u];
     }
-    for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+    for (; i < end; i += 256) acc ^= __builtin_nontemporal_load(src + i);
     out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
@@ -68,12 +73,15 @@ int peak_mfma_f16(float* out, int blocks, int iters, hipStream_t stream) {
     return (int)hipGetLastError();
 }
 
-// Enqueue the HBM read probe over src (device, n16 16-byte words).  out:
-// device, blocks * 256 uint32.  Returns 0 or a HIP error code.
-int peak_hbm_read(const void* src, long long n16, uint32_t* out, int blocks, hipStream_t stream) {
+// Enqueue the HBM read probe over src (device, n16 16-byte words), with
+// `unroll` (4, 8 or 16) loads per lane in flight.  out: device, blocks * 256
+// uint32.  Returns 0 or a HIP error code.
+int peak_hbm_read(const void* src, long long n16, uint32_t* out, int blocks, int unroll,
+                  hipStream_t stream) {
     if (!src || !out || n16 < 1 || blocks < 1) return -1;
-    hipLaunchKernelGGL(hbm_read_kernel, dim3(blocks), dim3(256), 0, stream, (const u4*)src,
-                       (int64_t)n16, out);
+    auto k = unroll >= 16 ? hbm_read_kernel<16> : unroll >= 8 ? hbm_read_kernel<8>
+                                                              : hbm_read_kernel<4>;
+    hipLaunchKernelGGL(k, dim3(blocks), dim3(256), 0, stream, (const u4*)src, (int64_t)n16, out);
     return (int)hipGetLastError();
 }
 

@@ -74,7 +74,9 @@ int main() {
     EXPECT(V::decode(P, P, P, P, 64, 8192, 28, 7, 128, 0.088f, 0, &n) == PASA_OK && n == 2);
     EXPECT(V::decode(P, P, P, P, 1, 100, 1, 1, 128, 0.088f, 1000, &n) == PASA_OK && n == 4);
     EXPECT(V::decode(P, P, P, P, 1, 100, 1, 1, 128, 0.088f, -1, &n) == PASA_ERR_INVALID);
-    EXPECT(V::decode(P, P, P, P, 1, 1 << 20, 1, 1, 128, 0.088f, 1, &n) == PASA_ERR_UNSUPPORTED);
+    // one split over a million keys: the running sum is folded into fp32 per segment
+    EXPECT(V::decode(P, P, P, P, 1, 1 << 20, 1, 1, 128, 0.088f, 1, &n) == PASA_OK && n == 1);
+    EXPECT(V::fwd(P, P, P, P, 1, 8, 131072, 8, 1, 128, 0.088f, 1) == PASA_OK);
     EXPECT(V::decode_workspace(nullptr, 1 << 20, 1, 1, 128, 1) == PASA_ERR_WORKSPACE);
     EXPECT(V::decode_workspace((char*)A + 4, 1 << 20, 1, 1, 128, 1) == PASA_ERR_WORKSPACE);
     EXPECT(V::decode_workspace(A, 767, 1, 1, 128, 1) == PASA_ERR_WORKSPACE);

@@ -10,8 +10,8 @@ runs the quick grid with assertions, and
 
     python -m tests.sweep [--full]
 
-prints one JSON line per grid point (the full grid reaches 65504 keys, the
-longest the fp16 running sum allows).
+prints one JSON line per grid point (the full grid reaches 131072 keys, twice
+the 65504 that one fp16 running sum could hold).
 
 What a point reports
   max_abs_s        largest |q.k| (unscaled) over the rows it was taken on
@@ -54,7 +54,8 @@ def points(full=False):
     """The grid: bias and amplitude sweeps, resonance amplitudes, sequence
     lengths and head dimensions."""
     pts = []
-    seqs = (1024, 4096, 16384, 65504) if full else (512,)   # 65504: the longest key range
+    # 65504 keys fill one fp16 running sum; 131072 spans four fp32-carried segments
+    seqs = (1024, 4096, 16384, 65504, 131072) if full else (512,)
     dims = (64, 128)
     for D in dims:
         for S in seqs:

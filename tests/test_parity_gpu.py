@@ -359,13 +359,15 @@ def test_binding_rejects_wrong_output_buffers(pasa):
 
 
 # ----------------------------------------------------------------- limits
-@pytest.mark.parametrize("causal", [False, True])
-def test_max_kv_length_flat_rows(pasa, causal):
-    """seqlen_kv = 65504, the most keys the fp16 running sum may hold: with
-    q = 0 every weight is 1, so the running sum reaches 65504 exactly and O is
-    the mean of the visible values."""
+@pytest.mark.parametrize("Skv,causal", [(65504, False), (65504, True), (131072, False),
+                                         (131072 + 77, True)])
+def test_long_kv_flat_rows(pasa, Skv, causal):
+    """q = 0: every weight is 1, so the running sum counts the visible keys
+    exactly and O is their values' mean.  65504 keys fill one fp16 sum to the
+    fp16 maximum's worth; beyond that the sum spans several 32768-key segments
+    carried in fp32."""
     import torch
-    Skv, Sq, D = 65504, 5, 128
+    Sq, D = 5, 128
     w = W.custom(1, Sq, Skv, 2, 1, D, causal, kind="normal", seed=65504)
     q, k, v = W.generate(w)
     q[:] = 0
@@ -373,8 +375,46 @@ def test_max_kv_length_flat_rows(pasa, causal):
     o, lse = pasa.attn_fwd(tq, tk, tv, causal=causal, scale=w.scale)
     torch.cuda.synchronize()
     ro, rl = attn_fp64(q, k, v, w.scale, causal)
-    check_o(o.cpu().numpy(), ro, v, label="flat 65504")
+    check_o(o.cpu().numpy(), ro, v, label=f"flat {Skv}")
     assert lse_ok(lse.cpu().numpy(), rl)
+
+
+@pytest.mark.parametrize("Sq,Skv,D,causal", [(131072, 131072, 128, True),
+                                             (2048, 131072 + 300, 64, False),
+                                             (1000, 100000, 128, False),
+                                             (70000, 70000, 64, True)])
+def test_long_kv_vs_oracle(pasa, Sq, Skv, D, causal):
+    """More keys than one fp16 running sum may hold (65504), biased inputs:
+    sampled rows against the oracle, every head gated."""
+    w = W.custom(1, Sq, Skv, 2, 1, D, causal, kind="bias", seed=Skv + D, bias=20.0)
+    say("long kv", Sq, Skv, D, causal)
+    (q, k, v), o, lse = run_fwd(pasa, w)
+    assert nonfinite(o) == 0 and nonfinite(lse) == 0
+    rng = np.random.default_rng(Skv)
+    rows = sample_rows(w, 256, rng)
+    # the last rows of a causal problem see the most keys
+    rows = np.unique(np.concatenate([rows, [h * Sq + Sq - 1 - i for h in range(2) for i in range(8)]]))
+    ro, rl = attn_fp64(q, k, v, w.scale, causal, rows=rows)
+    go, gl = gather_rows(o, lse, w, rows)
+    check_o(go, ro, v, heads=row_heads(w, rows), label=f"long kv {Sq}x{Skv} D{D}")
+    assert lse_ok(gl, rl)
+
+
+def test_decode_one_split_beyond_fp16_sum(pasa):
+    """One decode split over 200000 keys (the fp16 sum is folded into fp32 every
+    32768 keys) against the oracle, and against four splits."""
+    import torch
+    w = W.custom(2, 1, 200000, 8, 2, 128, False, kind="bias", seed=200, bias=20.0)
+    q, k, v = W.generate(w)
+    tq, tk, tv = to_gpu(q, k, v)
+    o1, l1 = pasa.attn_decode(tq, tk, tv, num_splits=1, scale=w.scale)
+    o4, l4 = pasa.attn_decode(tq, tk, tv, num_splits=4, scale=w.scale)
+    torch.cuda.synchronize()
+    ro, rl = attn_fp64(q, k, v, w.scale, False)
+    check_o(o1.cpu().numpy(), ro, v, label="decode 1 split 200000 keys")
+    check_o(o4.cpu().numpy(), ro, v, label="decode 4 splits 200000 keys")
+    assert lse_ok(l1.cpu().numpy(), rl[:, :, 0])
+    assert lse_ok(l4.cpu().numpy(), rl[:, :, 0])
 
 
 def test_decode_deterministic_and_matches_prefill_shape(pasa):

@@ -61,7 +61,10 @@ def test_fwd_validation(lib, name):
     assert _fwd(lib, name, causal=2) == -1
     assert _fwd(lib, name, D=96) == -2
     assert _fwd(lib, name, D=256) == -2
-    assert _fwd(lib, name, Skv=65505) == -2
+    # one head's K/V slab beyond the 4 GiB a buffer descriptor addresses
+    # (65505+ keys are accepted: the running sum is carried per segment)
+    assert _fwd(lib, name, Skv=1 << 24, Hq=1, D=128) == -2
+    assert _fwd(lib, name, Sq=2 ** 31 - 100) == -2   # rows past the int range of an item
     assert _fwd(lib, name, scale=0.0) == -2
     assert _fwd(lib, name, scale=float("nan")) == -2
     # more 256-row work items than an int counts (the tensors would not fit a GPU)

@@ -130,22 +130,11 @@ __device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 
     _Float16 mb;
     float off = 0.0f;
     if (!NAIVE) {
-        // four independent partial sums / maxima keep the dependency chains
-        // short; each starts from the sub-tile's first scores
-        float ps[4], pm[4];
+        // four independent partial maxima keep the dependency chains short;
+        // each starts from the sub-tile's first scores
+        float pm[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const bool on = full || vis(0, r);
-            ps[r] = on ? S[0][r] : 0.0f;
-            pm[r] = on ? S[0][r] : -__builtin_inff();
-        }
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int r = (t == 0 ? 4 : 0); r < 16; ++r) {
-                const bool on = full || vis(t, r);
-                ps[r & 3] += on ? S[t][r] : 0.0f;
-            }
+        for (int r = 0; r < 4; ++r) pm[r] = (full || vis(0, r)) ? S[0][r] : -__builtin_inff();
         // maxima two scores at a time (v_max3_f32 on the raw products: no
         // NaN canonicalisation is needed for them)
 #pragma unroll
@@ -164,10 +153,32 @@ __device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 
             for (int i = 0; i + 1 < NV; i += 2) pm[k] = max3f(pm[k], vv[i], vv[i + 1]);
             if (NV & 1) pm[k] = max3f(pm[k], vv[NV - 1], vv[NV - 1]);
         }
-        const float sum = xsum32((ps[0] + ps[1]) + (ps[2] + ps[3]));
         const float m32 = xmax32(max3f(pm[0], pm[1], max3f(pm[2], pm[3], pm[3])));
-        const float cmu = cnt > 0 ? r16(c * (sum / (float)cnt)) : st.R;
-        off = (st.R == -__builtin_inff()) ? cmu : fmaxf(cmu, st.R);
+        // The pseudo-average never exceeds the block maximum, so max(c*mu, R)
+        // is R wherever c*max <= R; the mean is formed only when some row of
+        // the wave has c*max above R (the margin covers the rounding of the
+        // mean's sum: at most 128 terms, each at most the maximum).  This
+        // gives the same offsets as always forming it.  The strict variant's
+        // fp16 rounding of c*mu can exceed c*max, so it always forms it.
+        const float cm = c * m32;
+        const bool may = cnt > 0 && !(cm + __builtin_fabsf(cm) * 0x1p-16f < st.R);
+        if (STRICT || wave_any(may)) {
+            float ps[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ps[r] = (full || vis(0, r)) ? S[0][r] : 0.0f;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = (t == 0 ? 4 : 0); r < 16; ++r) {
+                    const bool on = full || vis(t, r);
+                    ps[r & 3] += on ? S[t][r] : 0.0f;
+                }
+            const float sum = xsum32((ps[0] + ps[1]) + (ps[2] + ps[3]));
+            const float cmu = cnt > 0 ? r16(c * (sum / (float)cnt)) : st.R;
+            off = (st.R == -__builtin_inff()) ? cmu : fmaxf(cmu, st.R);
+        } else {
+            off = st.R;
+        }
         mb = fma_to_h(m32, c, -off);
         // refine: the tile's largest entries would sit where fp16 is coarse
         // (or overflow); centre the row at its own maximum instead

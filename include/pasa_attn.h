@@ -167,6 +167,33 @@ int pasa_attn_decode(const void* q, const void* k_cache, const void* v_cache, vo
                      size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pasa_attn_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * operation, arguments, split choice, kernels and results are pasa_attn_decode's
+ * (bit for bit, for the same num_splits); only the fp32 partials live in a
+ * scratch area the library reserves statically: PASA_DECODE_SCRATCH_BYTES
+ * (16 MiB) of device memory per GPU, held from the library's load until the
+ * process ends.  The call itself allocates nothing and frees nothing.
+ * Limit: the partials of the split count used,
+ * pasa_attn_decode_workspace_bytes(batch, num_heads_q, head_dim, n), must fit
+ * the scratch area (the decode workload of 64 sequences x 28 query heads x
+ * head_dim 128 at 2 splits takes 1.8 MB).
+ * Every call on one GPU uses that GPU's one scratch area: calls that overlap in
+ * time on one GPU (different streams or host threads without ordering between
+ * them) race and may return wrong results; calls on one stream are ordered and
+ * safe.  The area keeps the last call's partials; each call writes every
+ * partial it reads, so nothing needs clearing.
+ * Errors: as pasa_attn_decode, with PASA_ERR_WORKSPACE when the partials exceed
+ * PASA_DECODE_SCRATCH_BYTES, and PASA_ERR_HIP if the scratch area's device
+ * address cannot be obtained.
+ */
+#define PASA_DECODE_SCRATCH_BYTES (16u << 20)
+int pasa_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                             float* lse, int batch, int seqlen_kv, int num_heads_q, int gqa_group,
+                             int head_dim, float softmax_scale, int num_splits,
+                             hipStream_t stream);
+
+/*
  * Split-KV decode over a paged KV cache (one query token per sequence).  The
  * operation is pasa_attn_decode's: the same PASA tile numerics per split and
  * the same merge of the normalised partials ("Block Sparse Flash Attention"

@@ -35,6 +35,8 @@ _lib.pasa_attn_fwd_fp8.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, 
                                    _vp]
 _lib.pasa_attn_fwd_fp8.restype = _i
 _lib.pasa_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _vp]
+_lib.pasa_attn_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp]
+_lib.pasa_attn_decode_noalloc.restype = _i
 _lib.pasa_attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                                         _i, _f, _i, _vp, _sz, _vp]
 _lib.pasa_attn_decode_paged.restype = _i
@@ -224,6 +226,31 @@ def attn_decode(q, k_cache, v_cache, num_splits=0, scale=None, out=None, lse=Non
                                _stream(stream))
     _check(rc, "pasa_attn_decode")
     return (out, lse) if return_lse or lse is not None else out
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, out, lse=None, num_splits=0, scale=None,
+                        stream=None):
+    """attn_decode with the partials in the library's static per-GPU scratch
+    area (no device allocation by the library; out and lse are the caller's).
+    Calls that overlap in time on one GPU race for that area."""
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _want(t, nm)
+    if q.dim() != 4 or q.shape[1] != 1 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [B,1,Hq,D]; caches [B,Skv,Hkv,D]")
+    B, _, Hq, D = q.shape
+    Bk, Skv, Hkv, Dk = k_cache.shape
+    if Bk != B or Dk != D or Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError("inconsistent q/cache shapes")
+    if scale is None:
+        scale = D ** -0.5
+    _want_shape(out, "out", q.shape, torch.float16)
+    if lse is not None:
+        _want_shape(lse, "lse", (B, Hq), torch.float32)
+    rc = _lib.pasa_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+                                       B, Skv, Hq, Hq // Hkv, D, float(scale), int(num_splits),
+                                       _stream(stream))
+    _check(rc, "pasa_attn_decode_noalloc")
+    return out, lse
 
 
 def attn_decode_paged(q, k_pages, v_pages, block_table, seq_lens, num_splits=0, scale=None,

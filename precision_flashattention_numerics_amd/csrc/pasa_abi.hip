@@ -4,6 +4,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/pasa_attn.h"
 #include "kernels.hpp"
 #include "pasa_validate.hpp"
@@ -45,6 +47,32 @@ int decode_launch(const void* q, const void* k, const void* v, void* o, float* l
                                     stream) != hipSuccess)
         return PASA_ERR_HIP;
     return PASA_OK;
+}
+
+// Decode partials for callers that cannot allocate (pasa_attn_decode_noalloc):
+// a file-scope device array, one copy per GPU, held until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host it is only
+// a stand-in for the symbol); it resolves each device's address once, with
+// that device current, and uses that address.
+constexpr size_t kScratchBytes = PASA_DECODE_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices] = {};
+
+// The current device's copy of the scratch array, or nullptr on a HIP error.
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_addr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return nullptr;
+        scratch_addr[dev] = p;
+    }
+    return scratch_addr[dev];
 }
 
 }  // namespace
@@ -104,6 +132,24 @@ int pasa_attn_decode(const void* q, const void* k_cache, const void* v_cache, vo
     if (rc != PASA_OK) return rc;
     return decode_launch(q, k_cache, v_cache, o, lse, batch, seqlen_kv, num_heads_q, gqa_group,
                          head_dim, softmax_scale, n, workspace, nullptr, nullptr, 0, 0, 0, stream);
+}
+
+int pasa_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                             float* lse, int batch, int seqlen_kv, int num_heads_q, int gqa_group,
+                             int head_dim, float softmax_scale, int num_splits,
+                             hipStream_t stream) {
+    int n = 0;
+    const int rc = V::decode(q, k_cache, v_cache, o, batch, seqlen_kv, num_heads_q, gqa_group,
+                             head_dim, softmax_scale, num_splits, &n);
+    if (rc != PASA_OK) return rc;
+    if (V::workspace_bytes(batch, num_heads_q, head_dim, n) > kScratchBytes)
+        return PASA_ERR_WORKSPACE;
+    void* ws = device_scratch();
+    if (ws == nullptr) return PASA_ERR_HIP;
+    // every partial the combine reads is written by this call's split kernel
+    // (an empty split writes o = 0, lse = -inf), so nothing is cleared first
+    return decode_launch(q, k_cache, v_cache, o, lse, batch, seqlen_kv, num_heads_q, gqa_group,
+                         head_dim, softmax_scale, n, ws, nullptr, nullptr, 0, 0, 0, stream);
 }
 
 int pasa_attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,

@@ -231,14 +231,20 @@ def main():
     ap.add_argument("--full", action="store_true", help="the long grid (sequences to 65504)")
     ap.add_argument("--replay-only", action="store_true",
                     help="only the columns that need no GPU (scores, predicted overflow, refine rate)")
+    ap.add_argument("--part", default="0/1", metavar="K/N",
+                    help="run only grid points with index = K mod N (to split a long grid)")
     args = ap.parse_args()
+    k_part, n_part = (int(x) for x in args.part.split("/"))
     if args.replay_only:
         for n, pt in enumerate(points(args.full)):
-            print(json.dumps(replay(pt, seed=100 + n)), flush=True)
+            if n % n_part == k_part:
+                print(json.dumps(replay(pt, seed=100 + n)), flush=True)
         return
     import precision_flashattention_numerics_amd as pasa
     results = []
     for n, pt in enumerate(points(args.full)):
+        if n % n_part != k_part:
+            continue
         r = measure(pasa, pt, seed=100 + n)
         results.append(r)
         print(json.dumps(r), flush=True)

@@ -16,15 +16,15 @@
 //   taken relative to that instead
 //   R'    = max(R, off + m_b)      running maximum, log2 units        (fp32)
 //   s     = fp16(R' - off)                                            (fp16)
-//   X     = fp16_rne(c*S - (off + s)) (one rounding), masked keys -> -inf
+//   X     = fp16_rne(fp32(c*S - (off + s))), masked keys -> -inf
 //   P     = exp2(X);  r = sum_j P                                     (fp16)
 //   alpha = exp2(fp16(R - R'))                                        (fp16)
 //   (l_hi, l_lo) <- compensated fp16 sum of alpha*(l_hi, l_lo) + r    (fp16)
 //   every 32768 keys: l_c <- l_c + (l_hi + l_lo), (l_hi, l_lo) <- 0;
 //   l_c <- alpha*l_c on every block                                    (fp32)
 // where c = scale * log2(e).  X is the shifted tile fp16(c*S - off) moved
-// down by s, formed in a single rounding (s is known before the tile is
-// formed).  Because X is taken against off + s, P = exp2(c*S - R') up to
+// down by s, formed straight from the fp32 score (s is known before the tile
+// is formed).  Because X is taken against off + s, P = exp2(c*S - R') up to
 // rounding whatever off was: the shift changes only which fp16 numbers are
 // formed, never the softmax (a per-row shift leaves softmax unchanged).  The
 // epilogue recovers the exact log-sum-exp as ln2 * (R + log2(L)) with
@@ -187,8 +187,13 @@ __device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 
             mb = fma_to_h(m32, c, -off);
         }
         // the running maximum and s are known at this point, so the exponent
-        // argument (the shifted tile less s) is formed in one rounding:
-        // X = fp16(c*S - (off + s))
+        // argument (the shifted tile less s) is formed directly from the fp32
+        // score: X = fp16(fp32(c*S - (off + s))), an fp32 fused multiply-add
+        // and a packed round-to-nearest-even convert.  The fp32 step keeps 13
+        // bits more than fp16, so X equals the single rounding of the exact
+        // value except in rare near-ties, where it is one fp16 step off (in
+        // either direction).  Both instructions issue at a higher rate than the
+        // mixed-precision FMA that would round once.
         const float top = STRICT ? (float)((_Float16)off + mb) : off + (float)mb;
         const float Rn = cnt > 0 ? fmaxf(st.R, top) : st.R;
         const _Float16 s = cnt > 0 ? (_Float16)(Rn - off) : (_Float16)0;
@@ -197,7 +202,7 @@ __device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                h2 x = fma_to_h2(S[t][r], S[t][r + 1], c, noff);
+                h2 x = to_h2(__builtin_fmaf(S[t][r], c, noff), __builtin_fmaf(S[t][r + 1], c, noff));
                 if (!full) {
                     if (!vis(t, r)) x.x = kHalfNegInf;
                     if (!vis(t, r + 1)) x.y = kHalfNegInf;

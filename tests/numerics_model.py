@@ -14,7 +14,7 @@ differ in one step:
   fused         the kernels' rule: off = c*mu (first visible block) or
                 max(c*mu, R); m_b = fp16(c*max S - off), refine to the row
                 maximum when m_b > 4; R' = max(R, off + m_b); s = fp16(R' - off);
-                X = fp16(c*S - (off + s)) in one rounding
+                X = fp16(fp32(c*S - (off + s))) straight from the fp32 score
   fused_no_mu   the same with the pseudo-average replaced by the running
                 maximum: off = R, and on a row's first block the row maximum
   two_round     the shifted fp16 tile T = fp16(c*S - off) formed first, its
@@ -147,7 +147,9 @@ def emulate_rows(q_rows, k, v, scale, limits, block, variant="fused"):
             if two:
                 X = _h(T - s[:, None])
             else:
-                X = _h(c * S - (off + s).astype(F32).astype(np.float64)[:, None])
+                # fp32 fused multiply-add, then the round-to-nearest-even convert
+                z = (off + s).astype(F32).astype(np.float64)
+                X = _h((c * S - z[:, None]).astype(F32))
         X = np.where(vis, X.astype(np.float64), -np.inf)
         P = _h(np.exp2(X))
         r = _tree_sum(P)

@@ -4,7 +4,7 @@ the kernels (tests/numerics_model.py), against the binary64 oracle.
 "Online Pseudo-average Shifting Attention (PASA) ...", Abstract: the
 pseudo-average shift keeps the half-precision tile in range.  On matrix
 units that emit fp32 scores (CDNA's), the kernels form each fp16 exponent
-argument from the fp32 score in one rounding against the running maximum, so:
+argument straight from the fp32 score against the running maximum, so:
   * the pseudo-average only decides the base s is rounded against: on the
     biased inputs it is never selected (the running maximum dominates it) and
     the output is bit-identical without it; on unbiased inputs it moves the
@@ -83,8 +83,9 @@ def test_pseudo_average_moves_unbiased_rows_at_rounding_level():
 
 
 def test_two_rounding_tile_within_bar(qwen2_slice):
-    """Forming the shifted fp16 tile first and subtracting s in fp16 (two
-    roundings) stays within the bar as well; the kernels use one rounding."""
+    """Forming the shifted fp16 tile first and subtracting s in fp16 (two fp16
+    roundings) stays within the bar as well; the kernels form X straight from
+    the fp32 score."""
     w, sl = qwen2_slice
     _, _, e, le = _run(w, sl, "two_round")
     assert e <= REL_BAR and le <= LSE_BAR

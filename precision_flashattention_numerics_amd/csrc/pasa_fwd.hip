@@ -32,7 +32,7 @@
 //     staging registers; rows past the sequence end read as zero), stored
 //     row-major with XOR-swizzled 16-byte chunks.  V is consumed through the
 //     transposing LDS read of gfx950 (ds_read_b64_tr_b16).  Two LDS stages per
-//     tensor; each block's loads have two phases to land.
+//     tensor; a block's K loads have two phases to land, its V loads one.
 //   * Workgroups are ordered so that each XCD (each with its own L2) works on
 //     one key/value head at a time, and causal tiles are issued longest first.
 //   * Blocks that every row of a wave sees in full take a branch-free path;
@@ -316,13 +316,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __syncthreads();
 
     // Phase p: group 0 runs mphase(p/2) on even p and vphase(p/2) on odd p;
-    // group 1 runs one phase behind.  K(m+1) and V(m) are loaded during phases
-    // 2m and 2m+1 into the stages freed by K(m-1) and V(m-2).
+    // group 1 runs one phase behind.  K(m+1) is loaded from phase 2m and V(m)
+    // from phase 2m+1 (spreading the loads' issue over both phases), into the
+    // stages freed by K(m-1) and V(m-2); both have landed by the barrier that
+    // ends phase 2m+1, before either is read.
     const int nphase = nb0 > 0 ? 2 * nb0 + 2 : 0;   // nb0: the longer of the ranges
     for (int p = 0; p < nphase; ++p) {
         if ((p & 1) == 0) {
             const int m = p >> 1;
             if (m + 1 < nbl) load_k(m + 1);
+        } else {
+            const int m = p >> 1;
             if (m < nbl) load_v(m);
         }
         const int pp = p - grp;   // this group's own phase index

@@ -79,9 +79,13 @@ __device__ __forceinline__ h2 hmax(h2 a, h2 b) { return __builtin_elementwise_ma
 // repacking): the SDWA form of v_exp_f16 on the low halves, preserving the
 // high halves, then on the high halves, preserving the low results.  A
 // preserving write reads the register a transcendental instruction just
-// wrote, a read that needs wait states on this ISA; issuing the four low
-// halves first puts three instructions between each pair, and the trailing
-// s_nop covers the first consumer.
+// wrote.  The CDNA instruction-set guides' table of manually inserted wait
+// states asks for one wait state after a transcendental op whose result a
+// non-transcendental VALU op reads, and one after a sub-dword SDWA write
+// whose register a VALU op reads; the compiler's hazard recognizer does not
+// see inside inline asm.  Issuing the four low halves first puts three
+// instructions between each pair, and the trailing s_nop 1 (two wait states)
+// separates the last write from the first consumer after the block.
 __device__ __forceinline__ void hexp2_pk4(h2* r) {
     asm("v_exp_f16_sdwa %0, %0 dst_sel:WORD_0 dst_unused:UNUSED_PRESERVE src0_sel:WORD_0\n\t"
         "v_exp_f16_sdwa %1, %1 dst_sel:WORD_0 dst_unused:UNUSED_PRESERVE src0_sel:WORD_0\n\t"

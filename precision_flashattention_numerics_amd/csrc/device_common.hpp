@@ -66,13 +66,6 @@ __device__ __forceinline__ bool wave_any(bool p) {
 
 __device__ __forceinline__ _Float16 hexp2(_Float16 x) { return __builtin_elementwise_exp2(x); }
 
-__device__ __forceinline__ h2 hexp2(h2 x) {
-    h2 r;
-    r.x = __builtin_elementwise_exp2(x.x);
-    r.y = __builtin_elementwise_exp2(x.y);
-    return r;
-}
-
 __device__ __forceinline__ h2 hmax(h2 a, h2 b) { return __builtin_elementwise_max(a, b); }
 
 // exp2 of both halves of four packed pairs, in place (same registers, no
@@ -99,18 +92,8 @@ __device__ __forceinline__ void hexp2_pk4(h2* r) {
         : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
 }
 
-// fp16(c * a + z) for two fp32 values, one rounding each (fused multiply-add
-// in mixed precision, round-to-nearest-even), packed into one register.
-__device__ __forceinline__ h2 fma_to_h2(float a, float b, float c, float z) {
-    h2 t;
-    asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[0,0,0]\n\t"
-        "v_fma_mixhi_f16 %0, %4, %2, %3 op_sel_hi:[0,0,0]"
-        : "=&v"(t)
-        : "v"(a), "v"(c), "v"(z), "v"(b));
-    return t;
-}
-
-// fp16(c * a + z), the same single rounding as fma_to_h2.
+// fp16(c * a + z) for fp32 operands with one rounding (fused multiply-add in
+// mixed precision, round-to-nearest-even).
 __device__ __forceinline__ _Float16 fma_to_h(float a, float c, float z) {
     h2 t;
     asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[0,0,0]" : "=v"(t) : "v"(a), "v"(c), "v"(z));

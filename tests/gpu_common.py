@@ -7,14 +7,21 @@ confined to a few rows ("Online Pseudo-average Shifting Attention (PASA) ...",
 Abstract: RMSE against high-precision attention):
   * no inf/NaN in O;
   * relative RMSE over the whole output  <= REL_RMSE_MAX (2e-3);
-  * relative RMSE of every (batch, head)  <= REL_RMSE_MAX;
+  * relative RMSE of every (batch, head)  <= REL_RMSE_MAX, for heads with
+    at least MIN_ROWS_PER_HEAD rows in the comparison (a head of a decode
+    output is a single row and is gated as a row);
   * the worst row's relative error       <= ROW_REL_MAX (1e-2), where a row
     whose reference nearly cancels is measured against a quarter of the
     norm of a typical value row instead of its own norm.
 The row bound: the fp16 rounding of an output element is at most 2^-11
 relative, and the weights' fp16 roundings (exponent argument, exponential)
-move a row by a few 1e-4 on these inputs; 1e-2 leaves a wide margin while a
-single wrong 16-byte chunk (8 of 64 or 128 values) moves its row by 0.1 or more.
+move a row by a few 1e-4 on these inputs.  Where scores reach ~2e5 (the
+key-bias jump recipe) the matrix cores' fp32 accumulation of each score is
+off by a few 1e-2 in the score, i.e. a few 1e-3 in its weight, and a row
+whose weight is shared by two nearly tied keys carries that almost fully
+(up to ~2e-3 measured); a head's RMSE over many rows averages it out, a
+single row does not.  1e-2 leaves a wide margin while a single wrong 16-byte
+chunk (8 of 64 or 128 values) moves its row by 0.1 or more.
 """
 import sys
 
@@ -26,7 +33,7 @@ from workloads.metrics import (grouped_rel_rmse, lse_error, nonfinite, per_head_
 
 REL_RMSE_MAX = 2e-3      # relative RMSE of O against the binary64 oracle
 ROW_REL_MAX = 1e-2       # worst single row (see the module docstring)
-MIN_ROWS_PER_HEAD = 32   # sampled heads with fewer rows are reported, not gated
+MIN_ROWS_PER_HEAD = 32   # heads with fewer rows compared are reported, not gated
 
 
 def say(*a):
@@ -70,7 +77,7 @@ def check_o(o, ro, v, heads=None, label="", rel_max=REL_RMSE_MAX, row_max=ROW_RE
     rows = row_rel_err(o, ro, value_floor(v))
     if heads is None:
         ph = per_head_rel_rmse(o, ro).ravel()
-        gated = ph
+        gated = ph if o.shape[1] >= MIN_ROWS_PER_HEAD else np.zeros(0)
     else:
         g = grouped_rel_rmse(o, ro, heads)
         ph = np.array(list(g.values()))

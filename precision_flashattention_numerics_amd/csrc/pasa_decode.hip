@@ -89,7 +89,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
     const _Float16* vb = v + ((int64_t)b * Skv * Hkv + hkv) * D;
     const uint32_t slab_bytes =
         PAGED ? 0u : (uint32_t)(((int64_t)(Skv - 1) * kv_stride + D) * 2);
-    const i32x4 krs = make_rsrc(kb, slab_bytes);
+    const i32x4 krs = make_rsrc(kb, slab_bytes);   // contiguous: the whole slab
     const i32x4 vrs = make_rsrc(vb, slab_bytes);
 
     const int kbeg = min(split * split_len, Skv);
@@ -108,27 +108,46 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
         pchunk = ch;
     };
     if (PAGED) load_pages(0);
+    // the page (relative to pbase) and the sub-tile within it of the next
+    // sub-tile to issue; sub-tiles are issued in order, so both advance by
+    // counting instead of dividing by the page size
+    const int subs_per_page = PAGED ? pg.page_size / kSub : 1;
+    int next_page = 0, next_sub = PAGED ? (kbeg - pbase * pg.page_size) / kSub : 0;
+    const int64_t page_elems = PAGED ? (int64_t)pg.page_size * kv_stride : 0;
+
+    // paged: this wave's lane offsets inside a sub-tile and the segments'
+    // offsets inside a slot, computed once (measured about 5 % faster than
+    // forming them at each load, which the contiguous path does); the ring's
+    // LDS byte address
+    const TileDma<D, kSub, 1, false, false, true> kdma(stride_b, 0u, lane);
+    const TileDma<D, kSub, 1, true, false, true> vdma(stride_b, 0u, lane);
+    constexpr uint32_t kTileBytes = sub_halves<D>() * 2;   // one tensor's sub-tile
+    const uint32_t ring = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)smem);
 
     auto slot_k = [&](int j) { return smem + (j % kSlots) * 2 * sub_halves<D>(); };
     auto issue = [&](int j) {
-        _Float16* sk = slot_k(j);
+        const uint32_t slot = ring + (uint32_t)(j % kSlots) * (2 * kTileBytes);
         const int key0 = kbeg + j * kSub;
         if (PAGED) {
             // the sub-tile's page, and a descriptor over its rows that exist
-            const int pl = __builtin_amdgcn_readfirstlane(key0 / pg.page_size - pbase);
-            if (__builtin_amdgcn_readfirstlane(pl >> 6) != pchunk) load_pages(pl >> 6);   // rare
+            const int pl = next_page, sub = next_sub;
+            if (++next_sub == subs_per_page) {
+                next_sub = 0;
+                ++next_page;
+            }
+            if ((pl >> 6) != pchunk) load_pages(pl >> 6);   // rare
             const int page = __builtin_amdgcn_readlane(pcache, pl & 63);
             const int rows = min(kSub, Skv - key0);
             const bool ok = page >= 0 && page < pg.num_pages;
-            const int64_t base = ((int64_t)(ok ? page : 0) * pg.page_size + key0 % pg.page_size) *
-                                     kv_stride + (int64_t)hkv * D;
+            const int64_t base = (int64_t)(ok ? page : 0) * page_elems +
+                                 (int64_t)(sub * kSub) * kv_stride + (int64_t)hkv * D;
             const uint32_t bytes = ok ? (uint32_t)(((int64_t)(rows - 1) * kv_stride + D) * 2) : 0u;
-            stage_tile<D, kSub, 1, false, true>(make_rsrc(k + base, bytes), stride_b, 0, sk, 0, lane);
-            stage_tile<D, kSub, 1, true, true>(make_rsrc(v + base, bytes), stride_b, 0,
-                                         sk + sub_halves<D>(), 0, lane);
+            kdma.issue(make_rsrc(k + base, bytes), slot);
+            vdma.issue(make_rsrc(v + base, bytes), slot + kTileBytes);
         } else {
-            stage_tile<D, kSub, 1, false, true>(krs, stride_b, key0, sk, 0, lane);
-            stage_tile<D, kSub, 1, true, true>(vrs, stride_b, key0, sk + sub_halves<D>(), 0, lane);
+            _Float16* const sk = slot_k(j);
+            stage_tile_nt<D, kSub, false>(krs, stride_b, key0, sk, lane);
+            stage_tile_nt<D, kSub, true>(vrs, stride_b, key0, sk + sub_halves<D>(), lane);
         }
     };
 

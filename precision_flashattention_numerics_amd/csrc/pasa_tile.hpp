@@ -305,27 +305,15 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 }
 
 // One 16-byte-per-lane load from a buffer straight into LDS: lane l's bytes
-// land at lds + 16*l.  Issued as inline assembly on purpose: the compiler
-// would otherwise wait for every such load before any later LDS read (it
-// cannot tell the staging buffers apart); this kernel orders them itself with
-// an explicit vmcnt(0) wait and a barrier before the tile is consumed.
-// STREAM marks the load non-temporal (nt): for data read exactly once (the
-// decode KV cache), which streams from HBM markedly faster that way; tiles
-// that other workgroups re-read through L2 (prefill K/V) keep the default.
-template <bool STREAM = false>
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, const void* lds) {
+// land at lds + 16*l, non-temporal (nt: the data is read once).  Inline
+// assembly for the reason given at TileDma.
+__device__ __forceinline__ void dma16_nt(i32x4 rsrc, uint32_t voff, const void* lds) {
     const uint32_t la = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
-    if constexpr (STREAM)
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
-                     :
-                     : "v"(voff), "s"(rsrc), "s"(la)
-                     : "memory", "m0");
-    else
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                     :
-                     : "v"(voff), "s"(rsrc), "s"(la)
-                     : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(la)
+                 : "memory", "m0");
 }
 
 template <int D>
@@ -343,23 +331,24 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef short s4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s4 lds_s4;
 
-// Issue the loads of keys [row0, row0 + ROWS) of one head's K or V slab into
-// an LDS tile; the WAVES waves of the workgroup split the 1 KB segments.
-// stride_b = bytes between consecutive keys of the slab; STREAM as in dma16.
-template <int D, int ROWS, int WAVES, bool IS_V, bool STREAM = false>
-__device__ __forceinline__ void stage_tile(i32x4 rsrc, uint32_t stride_b, int row0,
-                                           _Float16* tile, int w, int lane) {
+// The loads of keys [row0, row0 + ROWS) of one head's K or V slab into an LDS
+// tile by one wave, non-temporal, with each lane's offset formed at the load
+// (TileDma's layout; stride_b = bytes between consecutive keys of the slab).
+// The contiguous decode stages its sub-tiles this way: measured against
+// TileDma's precomputed offsets, it streams the decode workload about 4 %
+// faster (the paged decode is the other way round).
+template <int D, int ROWS, bool IS_V>
+__device__ __forceinline__ void stage_tile_nt(i32x4 rsrc, uint32_t stride_b, int row0,
+                                              _Float16* tile, int lane) {
     constexpr int C = D / 8;
     constexpr int SEGS = ROWS * C / 64;          // 1 KB segments in the tile
-    static_assert(SEGS % WAVES == 0, "segments must split evenly over waves");
 #pragma unroll
-    for (int i = 0; i < SEGS / WAVES; ++i) {
-        const int seg = w * (SEGS / WAVES) + i;
+    for (int seg = 0; seg < SEGS; ++seg) {
         const int slot = seg * 64 + lane;
         const int row = slot / C, pos = slot % C;
         const int chunk = pos ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
         const uint32_t off = (uint32_t)(row0 + row) * stride_b + (uint32_t)chunk * 16u;
-        dma16<STREAM>(rsrc, off, tile + seg * 512);
+        dma16_nt(rsrc, off, tile + seg * 512);
     }
 }
 
@@ -377,15 +366,25 @@ __device__ __forceinline__ int swz_f8(int r) {
     return (r / (256 / D)) % C8;
 }
 
-// The staging of stage_tile with everything that does not change from one key block
-// to the next computed once, outside the key loop: each lane's byte offset
-// inside a block (row, swizzled chunk) and each of this wave's segments' LDS
-// byte offset inside a stage.  Per block the caller passes a descriptor that
-// starts at the block's first key (bounded by the slab end, so rows past the
-// sequence read as zero) and the stage's LDS byte address; issuing a segment
-// is then scalar moves and one load.  w_u is the wave index, wave-uniform.
-// F8: one-byte (e4m3) K tile in the fp8 layout above.
-template <int D, int ROWS, int WAVES, bool IS_V, bool F8 = false>
+// Staging of a ROWS-key tile straight from HBM into LDS (buffer_load ... lds,
+// no staging registers), split over WAVES waves in 1 KB segments (64 lanes x
+// 16 bytes; lane l's bytes land at the segment's LDS address + 16*l).
+// Everything that does not change from one key block to the next is computed
+// once, outside the key loop: each lane's byte offset inside a block (row,
+// swizzled chunk) and each of this wave's segments' LDS byte offset inside a
+// stage.  Per block the caller passes a descriptor that starts at the block's
+// first key (bounded by the data's end, so rows past it read as zero) and the
+// stage's LDS byte address; issuing a segment is then scalar moves and one
+// load.  The loads are inline assembly on purpose: the compiler would
+// otherwise wait for every such load before any later LDS read (it cannot
+// tell the stages apart); the kernels order them with explicit vmcnt waits
+// (and barriers where waves share a stage) before a stage is read.
+// w_u is the wave index, wave-uniform.  F8: one-byte (e4m3) K tile in the fp8
+// layout above.  STREAM marks the loads non-temporal (nt): for data read
+// exactly once (the decode's KV cache), which streams from HBM markedly faster
+// that way; tiles that other workgroups re-read through L2 (prefill K/V) keep
+// the default.
+template <int D, int ROWS, int WAVES, bool IS_V, bool F8 = false, bool STREAM = false>
 struct TileDma {
     static constexpr int C = F8 ? D / 16 : D / 8;   // 16-byte chunks per row
     static constexpr int SEGS = ROWS * C / 64;   // 1 KB segments in the tile
@@ -407,11 +406,18 @@ struct TileDma {
     }
     __device__ __forceinline__ void issue(i32x4 rsrc, uint32_t stage_lds) const {
 #pragma unroll
-        for (int i = 0; i < PER; ++i)
-            asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                         :
-                         : "v"(voff[i]), "s"(rsrc), "s"(stage_lds + lds[i])
-                         : "memory", "m0");
+        for (int i = 0; i < PER; ++i) {
+            if constexpr (STREAM)
+                asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                             :
+                             : "v"(voff[i]), "s"(rsrc), "s"(stage_lds + lds[i])
+                             : "memory", "m0");
+            else
+                asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                             :
+                             : "v"(voff[i]), "s"(rsrc), "s"(stage_lds + lds[i])
+                             : "memory", "m0");
+        }
     }
 };
 

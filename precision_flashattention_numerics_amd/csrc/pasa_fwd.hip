@@ -68,7 +68,11 @@ constexpr int fwd_smem_bytes() { return 2 /*stages*/ * 2 /*K,V*/ * tile_halves<D
 // Work item of workgroup L: (batch, query head, query tile).  Items are
 // enumerated key/value head by key/value head, longest causal tile first,
 // and dealt to XCDs so that each XCD holds one key/value head (or one slice
-// of one) at a time when the counts allow it.
+// of one) at a time when the counts allow it.  When they do not (the number
+// of key/value units neither divides nor is a multiple of the XCD count),
+// causal items go longest first across all units: with 12 units of the
+// Qwen2-shaped causal prefill (batch 3) that took 394 us against 460 us
+// unit by unit, bitwise-equal outputs.
 struct Item { int b, hq, tile; };
 __device__ __forceinline__ Item decode_item(int L, int N, int B, int Hq, int g, int nt, bool causal) {
     const int Hkv = Hq / g;
@@ -83,6 +87,12 @@ __device__ __forceinline__ Item decode_item(int L, int N, int B, int Hq, int g, 
         const int xcd = L % kXcds, k = L / kXcds;
         unit = (k / per_unit) * kXcds + xcd;
         item = k % per_unit;
+    } else if (causal) {
+        // no XCD grouping fits: longest tile first across all units (unit by
+        // unit, the last units' longest tiles would start last)
+        const int rank = L / (U * g), rem = L % (U * g);
+        unit = rem / g;
+        item = rank * g + rem % g;
     } else {
         unit = L / per_unit;
         item = L % per_unit;

@@ -57,3 +57,34 @@ def test_noalloc_refuses_partials_beyond_the_scratch_area():
     assert _noalloc(lib, q, k, k, o, lse, w, 8) == -3
     torch.cuda.synchronize()
     assert bool((o == 7.0).all())
+
+
+def test_noalloc_decode_in_a_graph_matches_eager():
+    """The callers the entry point is for include code under HIP graph
+    capture: captured once, every replay (with new inputs copied in, and eager
+    work and synchronisation between replays) reproduces the workspace decode
+    on those inputs bit for bit."""
+    import torch
+    import precision_flashattention_numerics_amd as pasa
+    lib = pasa.raw()
+    w = W.custom(4, 1, 3000, 14, 2, 128, False, kind="bias", seed=31, bias=25.0)
+    q, k, v = to_gpu(*W.generate(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.batch, w.heads_q), dtype=torch.float32, device="cuda")
+    assert _noalloc(lib, q, k, v, o, lse, w, 0) == 0   # first call on the device: outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rc = _noalloc(lib, q, k, v, o, lse, w, 0)
+    assert rc == 0
+    for rep in range(3):
+        w2 = W.custom(4, 1, 3000, 14, 2, 128, False, kind="bias", seed=40 + rep, bias=5.0 + 10 * rep)
+        q2, k2, v2 = to_gpu(*W.generate(w2))
+        q.copy_(q2); k.copy_(k2); v.copy_(v2)
+        ref_o, ref_l = pasa.attn_decode(q2, k2, v2, scale=w.scale)
+        torch.cuda.synchronize()
+        o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        say("noalloc graph replay", rep)
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_l)

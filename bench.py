@@ -100,11 +100,14 @@ def profile_cmd(set_name, kind):
 def source_hash():
     """sha256 over the kernel sources and the ABI header (what the counters
     describe), with comments and whitespace removed so that a comment edit
-    does not invalidate recorded counters."""
+    does not invalidate recorded counters, and over the compiler options the
+    library is built with."""
     import glob
     import hashlib
     import re
+    from precision_flashattention_numerics_amd import build as hip_build
     h = hashlib.sha256()
+    h.update(repr((hip_build.FLAGS, sorted(hip_build.SOURCE_FLAGS.items()))).encode())
     files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.hpp")))
     files.append(os.path.join(ROOT, "include", "pasa_attn.h"))
     for f in files:

@@ -6,6 +6,7 @@ fp32 arithmetic disabled (the compiler still emits packed fp16 math).
 import glob
 import os
 import subprocess
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -13,10 +14,20 @@ LIB = os.path.join(HERE, "libpasa_attn.so")
 ARCH = "gfx950"
 
 FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
+
+# Per-source compiler options.  The prefill kernels are scheduled with the
+# compiler's iterative ILP strategy: measured A/B in one process with
+# bitwise-equal outputs, the Qwen2-shaped prefill took 129.3 against 130.9 us
+# and the SVD-shaped one 295.8 against 302.0 us (the long-context one was
+# unchanged); the decode kernels measured 0.7 % slower with it and keep the
+# default.
+SOURCE_FLAGS = {
+    "pasa_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
 
 
 def sources():
@@ -28,12 +39,23 @@ PEAK_LIB = os.path.join(HERE, "peak", "libpasa_peak.so")
 
 
 def _hipcc(out, srcs, extra, verbose):
+    """Compile each source to an object with its own options, then link."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = out + ".tmp"
-    cmd = [hipcc, *FLAGS, *(extra or []), "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    with tempfile.TemporaryDirectory(prefix="pasa_build_") as d:
+        objs = []
+        for src in srcs:
+            obj = os.path.join(d, os.path.basename(src) + ".o")
+            cmd = [hipcc, *FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), *(extra or []),
+                   "-c", "-o", obj, src]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+            objs.append(obj)
+        cmd = [hipcc, *FLAGS, "-shared", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
     os.replace(tmp, out)
 
 

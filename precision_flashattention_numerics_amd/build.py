@@ -19,14 +19,14 @@ FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 
-# Per-source compiler options.  The prefill kernels are scheduled with the
-# compiler's iterative ILP strategy: measured A/B in one process with
-# bitwise-equal outputs, the Qwen2-shaped prefill took 129.3 against 130.9 us
-# and the SVD-shaped one 295.8 against 302.0 us (the long-context one was
-# unchanged); the decode kernels measured 0.7 % slower with it and keep the
-# default.
+# Per-source compiler options.  The head_dim-64 prefill kernels are scheduled
+# with the compiler's iterative minimum-register strategy: measured A/B in one
+# process with bitwise-equal outputs, 4-5 % faster on every head_dim-64 shape
+# tried (the SVD-shaped prefill 312.5 against 327.5 us).  At head_dim 128 the
+# strategies tried were within 1 % of the default or spilled registers in one
+# kernel, so it and the decode keep the default.
 SOURCE_FLAGS = {
-    "pasa_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "pasa_fwd_d64.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"],
 }
 
 

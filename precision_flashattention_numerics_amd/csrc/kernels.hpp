@@ -32,7 +32,11 @@ struct DecodeArgs {
 // Forward variants: PASA, PASA with fp16 running maximum and offset, the
 // naive fp16 Flash-Attention overflow exhibit, and PASA with e4m3 Q and K.
 enum { kVarPasa = 0, kVarStrict = 1, kVarNaive = 2, kVarFp8 = 3 };
-hipError_t launch_fwd(const FwdArgs& a, int variant, hipStream_t stream);
+hipError_t launch_fwd_d64(const FwdArgs& a, int variant, hipStream_t stream);
+hipError_t launch_fwd_d128(const FwdArgs& a, int variant, hipStream_t stream);
+inline hipError_t launch_fwd(const FwdArgs& a, int variant, hipStream_t stream) {
+    return a.head_dim == 128 ? launch_fwd_d128(a, variant, stream) : launch_fwd_d64(a, variant, stream);
+}
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream);
 // Same over a paged cache (a.k / a.v are the page pools, a.seqlen_kv the
 // longest key count the block table can address).

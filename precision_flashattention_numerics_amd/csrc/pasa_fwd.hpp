@@ -41,7 +41,10 @@
 //     free) LDS stages and writes whole rows with 16-byte stores.
 //
 // The per-block half-precision softmax (pseudo-average shift, refine, fp16
-// exponentials and sums) lives in pasa_tile.hpp.
+// exponentials and sums) lives in pasa_tile.hpp.  Each head dim is compiled
+// in its own translation unit (pasa_fwd_d64.hip, pasa_fwd_d128.hip), so that
+// the build can give each its own compiler scheduling options.
+#pragma once
 
 #include "kernels.hpp"
 #include "pasa_tile.hpp"
@@ -470,9 +473,5 @@ hipError_t launch_var(const FwdArgs& a, int variant, hipStream_t stream) {
 }
 
 }  // namespace
-
-hipError_t launch_fwd(const FwdArgs& a, int variant, hipStream_t stream) {
-    return a.head_dim == 128 ? launch_var<128>(a, variant, stream) : launch_var<64>(a, variant, stream);
-}
 
 }  // namespace pasa

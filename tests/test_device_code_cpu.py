@@ -28,7 +28,7 @@ from precision_flashattention_numerics_amd import build as B  # noqa: E402
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 pytestmark = pytest.mark.skipif(shutil.which(HIPCC) is None, reason="hipcc not available")
 
-KERNEL_SOURCES = ("pasa_fwd.hip", "pasa_decode.hip")
+KERNEL_SOURCES = ("pasa_fwd_d64.hip", "pasa_fwd_d128.hip", "pasa_decode.hip")
 
 
 @pytest.fixture(scope="module")
@@ -39,8 +39,8 @@ def asm(tmp_path_factory):
     for src in KERNEL_SOURCES:
         path = os.path.join(B.CSRC, src)
         dst = os.path.join(d, src + ".s")
-        subprocess.run([HIPCC, *flags, "-w", "--cuda-device-only", "-S", "-o", dst, path],
-                       check=True)
+        subprocess.run([HIPCC, *flags, *B.SOURCE_FLAGS.get(src, []), "-w", "--cuda-device-only",
+                        "-S", "-o", dst, path], check=True)
         out[src] = [l.split(";")[0].strip() for l in open(dst)]
     return out
 

@@ -34,7 +34,6 @@ struct DecodeArgs {
 enum { kVarPasa = 0, kVarStrict = 1, kVarNaive = 2, kVarFp8 = 3 };
 hipError_t launch_fwd_d64(const FwdArgs& a, int variant, hipStream_t stream);
 hipError_t launch_fwd_d128(const FwdArgs& a, int variant, hipStream_t stream);
-hipError_t launch_fwd_d128_naive(const FwdArgs& a, hipStream_t stream);
 inline hipError_t launch_fwd(const FwdArgs& a, int variant, hipStream_t stream) {
     return a.head_dim == 128 ? launch_fwd_d128(a, variant, stream) : launch_fwd_d64(a, variant, stream);
 }

@@ -19,21 +19,19 @@ FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 
-# Per-source compiler options (each prefill head dim is its own unit, and the
-# naive head_dim-128 exhibit one more), measured A/B in one process with
-# bitwise-equal outputs:
+# Per-source compiler options (each prefill head dim is its own unit),
+# measured A/B in one process with bitwise-equal outputs:
 #   * head_dim 64: the compiler's iterative minimum-register scheduling, 4-5 %
 #     faster on every head_dim-64 shape tried (the SVD-shaped prefill 312.5
 #     against 327.5 us);
-#   * head_dim 128 PASA kernels: the iterative ILP scheduling, about 1 % faster
-#     on the Qwen2-shaped prefill (129.3 against 130.9 us), unchanged on the
-#     long-context one; it spills registers in the naive key-split kernel,
-#     which therefore keeps the default;
+#   * head_dim 128 keeps the default: iterative ILP scheduling was 0.7-1.7 %
+#     faster on the Qwen2-shaped prefill but 0.6-2.1 % slower on the
+#     long-context one (and spilled registers in the naive key-split kernel);
+#     minimum-register was 0.5 % slower on the Qwen2 shape;
 #   * the decode keeps the default (0.7 % slower with iterative ILP, 11 %
 #     slower with minimum-register).
 SOURCE_FLAGS = {
     "pasa_fwd_d64.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"],
-    "pasa_fwd_d128.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
 
 

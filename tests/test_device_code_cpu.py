@@ -28,7 +28,7 @@ from precision_flashattention_numerics_amd import build as B  # noqa: E402
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 pytestmark = pytest.mark.skipif(shutil.which(HIPCC) is None, reason="hipcc not available")
 
-KERNEL_SOURCES = ("pasa_fwd_d64.hip", "pasa_fwd_d128.hip", "pasa_fwd_d128_naive.hip", "pasa_decode.hip")
+KERNEL_SOURCES = ("pasa_fwd_d64.hip", "pasa_fwd_d128.hip", "pasa_decode.hip")
 
 
 @pytest.fixture(scope="module")

@@ -34,7 +34,12 @@ __device__ __forceinline__ float xsum32(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 // max of three floats in one instruction; no NaN canonicalisation of the
-// inputs (the kernels feed it finite scores and -inf)
+// inputs (the kernels feed it finite scores and -inf).  It is inline assembly,
+// and the compiler's hazard recognizer does not look into inline assembly: a
+// read of a matrix product's result needs wait states after the product
+// (the compiler puts s_nop 11 before its own vector read of a 32x32x16
+// result), so where a product's result may reach max3f with no other
+// products issued in between, the caller passes it through xdl_fence first.
 __device__ __forceinline__ float max3f(float a, float b, float c) {
     float r;
     asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
@@ -58,6 +63,14 @@ __device__ __forceinline__ _Float16 xmax32(_Float16 x) {
     const _Float16 a = __builtin_bit_cast(_Float16, (unsigned short)r[0]);
     const _Float16 b = __builtin_bit_cast(_Float16, (unsigned short)r[1]);
     return a > b ? a : b;
+}
+
+// Orders every later read of x after 24 wait states (three s_nop 7): the
+// asm takes x as an in/out operand, so the compiler issues it after the
+// product that writes x and every use of x after it.  24 covers the compiler's
+// own 12 for a 32x32x16 fp16 result with room for the longer fp8 product.
+__device__ __forceinline__ void xdl_fence(f16v& x) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
 }
 
 __device__ __forceinline__ bool wave_any(bool p) {

@@ -52,8 +52,15 @@ struct Paging {
     int page_size, max_pages, num_pages;
 };
 
+// At head_dim 64 the register budget is capped at 256 (two waves per SIMD):
+// the kernel then needs 132 registers and keeps its accumulator in ordinary
+// vector registers, where the uncapped build moved it through AGPRs on every
+// sub-tile (batch 64, 28/4 heads, 8192 keys: 112.5 -> 98.3 us; batch 8,
+// 32/8 heads, 16384 keys: 62.8 -> 55.9 us; bitwise-equal outputs).  At
+// head_dim 128 the same cap measured slower on long caches and is not used.
 template <int D, bool PAGED>
-__global__ __launch_bounds__(64) void decode_split_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 10)))
+void decode_split_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
     const _Float16* __restrict__ v, float* __restrict__ o_part, float* __restrict__ lse_part,
     int Skv, int Hq, int group, float c, int split_len, int head_chunks, int nsplit, Paging pg) {
@@ -188,6 +195,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(
         if (j > 0 && j % (kSegKeys / kSub) == 0) fold_segment(st);
         f16v S[1];
         S[0] = qk_subtile_sw<D>(Ks, 0, qreg, n, hh);
+        xdl_fence(S[0]);   // the softmax's maxima read the product directly
         const int wbase = kbeg + j * kSub;
         const bool full = wbase + kSub <= kend;
         const int cnt = full ? kSub : kend - wbase;

@@ -285,8 +285,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                 pv_chunks_tr<D, 2 * NT>(Vs, 0, P, acc, lane);
             }
             if (qk) {
+                // no P V products follow these (first block): fence the
+                // results before the vector phase's maxima read them
 #pragma unroll
-                for (int t = 0; t < NT; ++t) S[t] = qk_sub(Ks, 32 * t);
+                for (int t = 0; t < NT; ++t) {
+                    S[t] = qk_sub(Ks, 32 * t);
+                    xdl_fence(S[t]);
+                }
             }
         }
         __builtin_amdgcn_s_setprio(0);

@@ -10,7 +10,12 @@ GPU): properties the sources rely on but the compiler could silently break.
 * no scratch memory (register spills would put stack traffic in the loop),
 * M0 is written only by the kernels' own LDS-DMA sequences and read by nothing
   else: those sequences set M0 in inline assembly, which is sound only while
-  the compiler keeps no value of its own in M0.
+  the compiler keeps no value of its own in M0,
+* every vector instruction inside inline assembly that reads a matrix
+  product's result comes at least 19 wait states after the product: the
+  compiler's hazard recognizer does not look into inline assembly, so the
+  sources keep such reads apart (by the products between them, or by an
+  explicit fence).
 """
 import os
 import re
@@ -42,6 +47,7 @@ def asm(tmp_path_factory):
         subprocess.run([HIPCC, *flags, *B.SOURCE_FLAGS.get(src, []), "-w", "--cuda-device-only",
                         "-S", "-o", dst, path], check=True)
         out[src] = [l.split(";")[0].strip() for l in open(dst)]
+        out["raw:" + src] = [l.rstrip("\n") for l in open(dst)]
     return out
 
 
@@ -91,3 +97,62 @@ def test_m0_only_in_lds_dma(asm, src):
         else:
             raise AssertionError(f"M0 used outside the LDS-DMA sequences: {l}")
     assert n_dma > 0
+
+
+MFMA_DST = re.compile(r"^v_mfma\S*\s+v\[(\d+):(\d+)\]")
+VREG = re.compile(r"\bv(\d+)\b|\bv\[(\d+):(\d+)\]")
+
+
+def _vregs(operands):
+    regs = set()
+    for m in VREG.finditer(operands):
+        if m.group(1) is not None:
+            regs.add(int(m.group(1)))
+        else:
+            regs.update(range(int(m.group(2)), int(m.group(3)) + 1))
+    return regs
+
+
+@pytest.mark.parametrize("src", KERNEL_SOURCES)
+def test_inline_asm_reads_of_products_wait(asm, src):
+    """Walk back from each vector instruction inside an inline-asm block over
+    the preceding instructions (in program text order, counting s_nop N as N+1
+    wait states and any other instruction as one) and require 19 wait states
+    after a product whose destination it reads."""
+    raw = asm["raw:" + src]
+    inside = False
+    seq = []   # (text, in_asm)
+    for line in raw:
+        if "#ASMSTART" in line:
+            inside = True
+            continue
+        if "#ASMEND" in line:
+            inside = False
+            continue
+        t = line.split(";")[0].strip()
+        if not t or t.startswith(".") or t.endswith(":"):
+            continue
+        seq.append((t, inside))
+    bad = []
+    for i, (t, in_asm) in enumerate(seq):
+        if not in_asm or not t.startswith("v_") or t.startswith("v_mfma"):
+            continue
+        parts = t.split(None, 1)
+        ops = parts[1].split(",") if len(parts) > 1 else []
+        srcs = _vregs(",".join(ops[1:]))
+        # an SDWA op preserving the other half also reads its destination
+        if "UNUSED_PRESERVE" in t:
+            srcs |= _vregs(ops[0])
+        waits = 0
+        for j in range(i - 1, -1, -1):
+            u = seq[j][0]
+            m = MFMA_DST.match(u)
+            if m and srcs & set(range(int(m.group(1)), int(m.group(2)) + 1)):
+                if waits < 19:
+                    bad.append((t, u, waits))
+                break
+            n = re.match(r"s_nop\s+(\d+)", u)
+            waits += int(n.group(1)) + 1 if n else 1
+            if waits >= 19:
+                break
+    assert not bad, bad[:5]

@@ -15,7 +15,11 @@ GPU): properties the sources rely on but the compiler could silently break.
   product's result comes at least 19 wait states after the product: the
   compiler's hazard recognizer does not look into inline assembly, so the
   sources keep such reads apart (by the products between them, or by an
-  explicit fence).
+  explicit fence),
+* every buffer load inside inline assembly (the LDS-DMA sequences) comes at
+  least 5 wait states after a vector instruction that writes one of its
+  scalar operands (v_readlane / v_readfirstlane and the like), for the same
+  reason.
 """
 import os
 import re
@@ -155,4 +159,57 @@ def test_inline_asm_reads_of_products_wait(asm, src):
             waits += int(n.group(1)) + 1 if n else 1
             if waits >= 19:
                 break
+    assert not bad, bad[:5]
+
+
+SREG = re.compile(r"\bs(\d+)\b|\bs\[(\d+):(\d+)\]")
+
+
+def _sregs(operands):
+    regs = set()
+    for m in SREG.finditer(operands):
+        if m.group(1) is not None:
+            regs.add(int(m.group(1)))
+        else:
+            regs.update(range(int(m.group(2)), int(m.group(3)) + 1))
+    return regs
+
+
+@pytest.mark.parametrize("src", KERNEL_SOURCES)
+def test_inline_asm_buffer_loads_after_valu_sgpr_writes(asm, src):
+    raw = asm["raw:" + src]
+    inside = False
+    seq = []
+    for line in raw:
+        if "#ASMSTART" in line:
+            inside = True
+            continue
+        if "#ASMEND" in line:
+            inside = False
+            continue
+        t = line.split(";")[0].strip()
+        if not t or t.startswith(".") or t.endswith(":"):
+            continue
+        seq.append((t, inside))
+    checked, bad = 0, []
+    for i, (t, in_asm) in enumerate(seq):
+        if not in_asm or not t.startswith("buffer_load"):
+            continue
+        checked += 1
+        srcs = _sregs(t.split(None, 1)[1])
+        waits = 0
+        for j in range(i - 1, -1, -1):
+            u = seq[j][0]
+            if u.startswith("v_"):
+                ops = u.split(None, 1)
+                dst = ops[1].split(",")[0] if len(ops) > 1 else ""
+                if _sregs(dst) & srcs:
+                    if waits < 5:
+                        bad.append((t, u, waits))
+                    break
+            n = re.match(r"s_nop\s+(\d+)", u)
+            waits += int(n.group(1)) + 1 if n else 1
+            if waits >= 5:
+                break
+    assert checked > 0
     assert not bad, bad[:5]

@@ -77,13 +77,14 @@ inline int fp8_scales(float q_scale, float k_scale, float softmax_scale) {
 
 // pasa_attn_decode_splits: waves on 256 CUs, measured: at head_dim 128 two
 // per CU (LDS would hold three, but fewer and longer key streams per sequence
-// read the cache faster); at head_dim 64 three per CU (of the six LDS holds).
+// read the cache faster); at head_dim 64 six per CU (the LDS limit) when there
+// are at least 256 (sequence, key/value head) units, else three.
 inline int decode_splits(int batch, int seqlen_kv, int num_heads_q, int gqa_group, int head_dim) {
     if (batch < 1 || seqlen_kv < 1 || num_heads_q < 1 || gqa_group < 1 ||
         num_heads_q % gqa_group != 0 || (head_dim != 64 && head_dim != 128))
         return 0;
     const int64_t units = (int64_t)batch * (num_heads_q / gqa_group) * ((gqa_group + 31) / 32);
-    const int64_t target = head_dim == 64 ? 768 : 512;
+    const int64_t target = head_dim == 64 ? (units >= 256 ? 1536 : 768) : 512;
     int64_t n = (target + units - 1) / units;
     const int64_t blocks = ((int64_t)seqlen_kv + kDecodeBlock - 1) / kDecodeBlock;
     if (n > blocks) n = blocks;

@@ -79,7 +79,8 @@ def test_decode_validation_and_sizes(lib):
     assert ws == ((rows * 128 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
     assert lib.pasa_attn_decode_workspace_bytes(0, 28, 128, 4) == 0
     assert lib.pasa_attn_decode_splits(64, 8192, 28, 7, 128) == 2   # 512 waves over 256 units
-    assert lib.pasa_attn_decode_splits(64, 8192, 28, 7, 64) == 3    # 768 waves
+    assert lib.pasa_attn_decode_splits(64, 8192, 28, 7, 64) == 6    # 1536 waves over 256 units
+    assert lib.pasa_attn_decode_splits(8, 16384, 32, 4, 64) == 12   # 768 waves over 64 units
     assert lib.pasa_attn_decode_splits(1, 100, 1, 1, 128) == 4      # four 32-key sub-tiles
     assert lib.pasa_attn_decode_splits(1, 20, 1, 1, 64) == 1
     assert lib.pasa_attn_decode_splits(1, 8192, 28, 3, 128) == 0    # 28 % 3 != 0

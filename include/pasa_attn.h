@@ -227,9 +227,11 @@ int pasa_attn_decode_paged(const void* q, const void* k_pages, const void* v_pag
 
 /* The split count pasa_attn_decode and pasa_attn_decode_paged use for
  * num_splits = 0 (host function, no device work): enough (sequence, key/value
- * head, split) work items for two waves per compute unit at head_dim 128 and
- * three at head_dim 64, clamped to the number of 32-key sub-tiles.  Returns 0
- * on invalid sizes, including a head_dim other than 64 or 128. */
+ * head, split) work items for two waves per compute unit at head_dim 128; at
+ * head_dim 64 six per compute unit when there are at least 256 (sequence,
+ * key/value head) pairs and three otherwise; clamped to the number of 32-key
+ * sub-tiles.  Returns 0 on invalid sizes, including a head_dim other than 64
+ * or 128. */
 int pasa_attn_decode_splits(int batch, int seqlen_kv, int num_heads_q, int gqa_group,
                             int head_dim);
 

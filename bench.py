@@ -23,8 +23,10 @@ kernel's overflow on each; relative RMSE of sampled output rows against the
 binary64 oracle; and the oracle itself timed on this host's cores over a
 bounded row sample (`cpu_baseline`).
 
-`--profile-config c3|c4` runs only that prefill workload (for rocprofv3), and
-`--summarize-profile DIR SET` writes the text summaries under profiles/.
+`--profile-config c3|c4` runs only that prefill workload, `--profile-config
+c5paged` only the decode over the shuffled 64-key-page cache (both for
+rocprofv3), and `--summarize-profile DIR SET` writes the text summaries under
+profiles/.
 """
 import argparse
 import json
@@ -50,6 +52,7 @@ K_STRICT = "fwd_kernelILi128ELb1ELi1ELb0E"   # strict PASA prefill, same shape
 K_NAIVE = "fwd_kernelILi128ELb1ELi2ELb0E"    # naive fp16 prefill, same shape
 K_C3 = "fwd_kernelILi64ELb0ELi0ELb1E"        # PASA prefill, head_dim 64, non-causal, key split
 K_SPLIT = "decode_split_kernelILi128ELb0E"   # decode split, head_dim 128, contiguous cache
+K_SPLIT_PAGED = "decode_split_kernelILi128ELb1E"   # decode split, head_dim 128, paged cache
 K_COMBINE = "decode_combine_kernel"
 
 # Profile sets: which bench invocation each rocprofv3 run wraps, and the file
@@ -59,17 +62,22 @@ PROFILE_SETS = {
         stem="pasa_prefill_qwen2shape_s4096_decode_b64_kv8192", config="c2",
         trace_args="--steps 20 --warmup 5 --no-cpu-baseline --no-other-configs",
         pmc_args="--steps 3 --warmup 1 --warm-seconds 0 --no-cpu-baseline --no-other-configs",
-        prefill=K_PREFILL, decode=True),
+        prefill=K_PREFILL, decode=K_SPLIT),
     "svd": dict(
         stem="pasa_prefill_svdshape_b2_s9216_d64", config="c3",
         trace_args="--profile-config c3 --steps 100",
         pmc_args="--profile-config c3 --steps 3 --warm-seconds 0",
-        prefill=K_C3, decode=False),
+        prefill=K_C3, decode=None),
     "longctx": dict(
         stem="pasa_prefill_longctx_s32768_h32_8_d128", config="c4",
         trace_args="--profile-config c4 --steps 20",
         pmc_args="--profile-config c4 --steps 2 --warm-seconds 0",
-        prefill=K_PREFILL, decode=False),
+        prefill=K_PREFILL, decode=None),
+    "paged": dict(
+        stem="pasa_decode_paged64_shuffled_b64_kv8192", config="c5",
+        trace_args="--profile-config c5paged --steps 100",
+        pmc_args="--profile-config c5paged --steps 3 --warm-seconds 0",
+        prefill=None, decode=K_SPLIT_PAGED),
 }
 PMC_SETS = {
     "pmc1": "SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_VMEM "
@@ -177,6 +185,8 @@ def summarize_profile(d, set_name):
         raise KeyError(sub)
     title = {"c2": "the Qwen2-7B-shaped causal prefill (batch 1, seq 4096, 28 query / 4 kv heads, "
                    "head_dim 128) and split-KV decode (batch 64, kv length 8192, 28/4 heads, head_dim 128)",
+             "c5": "the split-KV decode (batch 64, kv length 8192, 28/4 heads, head_dim 128) over a paged "
+                   "cache of 64-key pages in a seeded shuffled order",
              "c3": "the Stable-Video-Diffusion-shaped resonance prefill (batch 2, seq 9216, 5 heads, "
                    "head_dim 64, non-causal)",
              "c4": "the long-context causal prefill (batch 1, seq 32768, 32 query / 8 kv heads, "
@@ -185,14 +195,15 @@ def summarize_profile(d, set_name):
              "# command: " + profile_cmd(set_name, "trace"),
              f"# kernel sources sha256: {source_hash()}",
              "kernel                         calls  avg_us    min_us    max_us   algorithmic    rate"]
-    pre = st(ps["prefill"])
-    avg_p = float(pre["AverageNs"]) * 1e-3
-    lines.append(f"pasa prefill                 {int(pre['Calls']):6d} {avg_p:8.2f} "
-                 f"{float(pre['MinNs'])*1e-3:8.2f} {float(pre['MaxNs'])*1e-3:8.2f}  "
-                 f"{wp.flops():.4e} flop  {wp.flops()/avg_p/1e6:8.1f} TFLOP/s "
-                 f"({wp.flops()/avg_p/1e6/PEAK_FP16_TFLOPS:.3f} of 2500)")
+    if ps["prefill"]:
+        pre = st(ps["prefill"])
+        avg_p = float(pre["AverageNs"]) * 1e-3
+        lines.append(f"pasa prefill                 {int(pre['Calls']):6d} {avg_p:8.2f} "
+                     f"{float(pre['MinNs'])*1e-3:8.2f} {float(pre['MaxNs'])*1e-3:8.2f}  "
+                     f"{wp.flops():.4e} flop  {wp.flops()/avg_p/1e6:8.1f} TFLOP/s "
+                     f"({wp.flops()/avg_p/1e6/PEAK_FP16_TFLOPS:.3f} of 2500)")
     if ps["decode"]:
-        sp = st(K_SPLIT)
+        sp = st(ps["decode"])
         avg_s = float(sp["AverageNs"]) * 1e-3
         cb = st(K_COMBINE)
         avg_c = float(cb["AverageNs"]) * 1e-3
@@ -224,9 +235,6 @@ def summarize_profile(d, set_name):
         cf = _pick(cfetch, "copyBuffer")["FETCH_SIZE"] * 1024
         cw = _pick(cwrite, "copyBuffer")["WRITE_SIZE"] * 1024
         ff, wf = copy_bytes / cf, copy_bytes / cw
-        pf = _pick(fetch, ps["prefill"])["FETCH_SIZE"]
-        pw = _pick(write, ps["prefill"])["WRITE_SIZE"]
-        p_bytes = int(pf * 1024 * ff + pw * 1024 * wf)
         t = ["# HBM traffic per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),",
              "# each scaled by what the same counter reads for a plain 1 GiB device-to-device copy.",
              "# commands:",
@@ -235,13 +243,17 @@ def summarize_profile(d, set_name):
              f"source_sha256={source_hash()}",
              f"copy_bytes={copy_bytes}",
              f"copy_fetch_kib={cf/1024:.1f}", f"copy_write_kib={cw/1024:.1f}",
-             f"fetch_factor={ff:.4f}", f"write_factor={wf:.4f}",
-             f"prefill_fetch_kib={pf:.1f}", f"prefill_write_kib={pw:.1f}",
-             f"prefill_traffic_bytes={p_bytes}",
-             f"prefill_algorithmic_bytes={wp.io_bytes()}"]
+             f"fetch_factor={ff:.4f}", f"write_factor={wf:.4f}"]
+        if ps["prefill"]:
+            pf = _pick(fetch, ps["prefill"])["FETCH_SIZE"]
+            pw = _pick(write, ps["prefill"])["WRITE_SIZE"]
+            p_bytes = int(pf * 1024 * ff + pw * 1024 * wf)
+            t += [f"prefill_fetch_kib={pf:.1f}", f"prefill_write_kib={pw:.1f}",
+                  f"prefill_traffic_bytes={p_bytes}",
+                  f"prefill_algorithmic_bytes={wp.io_bytes()}"]
         if ps["decode"]:
-            sf = _pick(fetch, K_SPLIT)["FETCH_SIZE"]
-            sw = _pick(write, K_SPLIT)["WRITE_SIZE"]
+            sf = _pick(fetch, ps["decode"])["FETCH_SIZE"]
+            sw = _pick(write, ps["decode"])["WRITE_SIZE"]
             s_bytes = int(sf * 1024 * ff + sw * 1024 * wf)
             t += [f"decode_split_fetch_kib={sf:.1f}", f"decode_split_write_kib={sw:.1f}",
                   f"decode_split_traffic_bytes={s_bytes}",
@@ -255,7 +267,8 @@ def summarize_profile(d, set_name):
             continue
         c = _counters(path)
         rows.append(f"# {title2}: " + profile_cmd(set_name, key))
-        kernels = [("pasa prefill", ps["prefill"])] + ([("pasa decode split", K_SPLIT)] if ps["decode"] else [])
+        kernels = ([("pasa prefill", ps["prefill"])] if ps["prefill"] else []) + \
+            ([("pasa decode split", ps["decode"])] if ps["decode"] else [])
         for name, sub in kernels:
             vals = _pick(c, sub)
             rows.append(f"{name}: " + ", ".join(f"{k}={v:.0f}" for k, v in sorted(vals.items())))
@@ -282,7 +295,7 @@ def parse():
                          "that the c2 kernel's averages are its own")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--profile-config", choices=("c3", "c4"), default=None,
+    ap.add_argument("--profile-config", choices=("c3", "c4", "c5paged"), default=None,
                     help="run only this prefill workload: --steps launches after the warmup")
     ap.add_argument("--summarize-profile", nargs=2, metavar=("DIR", "SET"), default=None,
                     help="write the text summaries under profiles/ from a rocprofv3 output "
@@ -395,12 +408,47 @@ def measure_peaks(stream):
                    f"({shape[0]} workgroups of 256 per CU, {shape[1]} loads in flight per lane)"}
 
 
+def paged_pool(wd, tk, tv):
+    """The decode workload's cache (tk, tv [B, Skv, Hkv, D]) as a pool of 64-key
+    pages scattered in a seeded random order: (k pool, v pool, block table,
+    sequence lengths)."""
+    import numpy as np
+    import torch
+    ps = 64
+    n_pages = wd.batch * wd.seqlen_kv // ps
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(n_pages).astype(np.int32)).cuda()
+    kpool = torch.empty((n_pages, ps, wd.heads_kv, wd.head_dim), dtype=torch.float16, device="cuda")
+    vpool = torch.empty_like(kpool)
+    kpool[perm.long()] = tk.reshape(n_pages, ps, wd.heads_kv, wd.head_dim)
+    vpool[perm.long()] = tv.reshape(n_pages, ps, wd.heads_kv, wd.head_dim)
+    table = perm.reshape(wd.batch, wd.seqlen_kv // ps).contiguous()
+    lens = torch.full((wd.batch,), wd.seqlen_kv, dtype=torch.int32, device="cuda")
+    return kpool, vpool, table, lens
+
+
 def profile_only(args):
-    """--profile-config: one prefill workload alone, --steps launches after the
-    warmup, for rocprofv3 runs of that workload."""
+    """--profile-config: one prefill workload (or the paged decode) alone,
+    --steps launches after the warmup, for rocprofv3 runs of that workload."""
     import torch
     import precision_flashattention_numerics_amd as pasa
     import workloads as W
+    if args.profile_config == "c5paged":
+        wd = W.CONFIGS["c5"]
+        tq, tk, tv = (torch.from_numpy(x).cuda() for x in W.generate(wd))
+        kpool, vpool, table, lens = paged_pool(wd, tk, tv)
+        del tk, tv
+        od, ld = pasa.attn_decode_paged(tq, kpool, vpool, table, lens, scale=wd.scale)
+
+        def paged():
+            pasa.attn_decode_paged(tq, kpool, vpool, table, lens, scale=wd.scale, out=od, lse=ld)
+        n_warm, s_warm = warm(paged, args.warm_seconds, args.warmup)
+        med, _ = timed_batches(paged, args.steps, 1, torch.cuda.current_stream())
+        gbps = wd.io_bytes() / (med * 1e-3) / 1e9
+        print(json.dumps({"config": "c5 paged (64-key pages, shuffled)", "launches": args.steps,
+                          "ms": round(med, 5), "GBps": round(gbps, 1),
+                          "frac": round(gbps / PEAK_HBM_GBPS, 4), "warmup_launches": n_warm,
+                          "warmup_seconds": round(s_warm, 3)}), flush=True)
+        return
     w = W.CONFIGS[args.profile_config]
     tq, tk, tv = (torch.from_numpy(x).cuda() for x in W.generate(w))
     o = torch.empty_like(tq)
@@ -592,15 +640,7 @@ def main():
             torch.cuda.empty_cache()
         # the decode workload over a paged cache: 64-key pages scattered over
         # the pool in a seeded random order (HBM-bound like the contiguous one)
-        ps = 64
-        n_pages = wd.batch * wd.seqlen_kv // ps
-        perm = torch.from_numpy(np.random.default_rng(5).permutation(n_pages).astype(np.int32)).cuda()
-        kpool = torch.empty((n_pages, ps, wd.heads_kv, wd.head_dim), dtype=torch.float16, device="cuda")
-        vpool = torch.empty_like(kpool)
-        kpool[perm.long()] = tkd.reshape(n_pages, ps, wd.heads_kv, wd.head_dim)
-        vpool[perm.long()] = tvd.reshape(n_pages, ps, wd.heads_kv, wd.head_dim)
-        table = perm.reshape(wd.batch, wd.seqlen_kv // ps).contiguous()
-        lens = torch.full((wd.batch,), wd.seqlen_kv, dtype=torch.int32, device="cuda")
+        kpool, vpool, table, lens = paged_pool(wd, tkd, tvd)
         opg, lpg = pasa.attn_decode_paged(tqd, kpool, vpool, table, lens, scale=wd.scale)
 
         def paged():

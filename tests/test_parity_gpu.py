@@ -277,6 +277,24 @@ def test_decode_shapes_vs_oracle(pasa, Skv, n, Hq, Hkv, D):
     assert lse_ok(lse.cpu().numpy(), rl[:, :, 0])
 
 
+@pytest.mark.parametrize("B,Skv,Hq,Hkv,D,splits", [(64, 1500, 28, 4, 64, 6), (16, 700, 32, 32, 64, 3),
+                                                    (8, 3000, 32, 8, 64, 12)])
+def test_decode_default_splits_head_dim_64_vs_oracle(pasa, B, Skv, Hq, Hkv, D, splits):
+    """The library's split count at head_dim 64 (six waves per CU from 256
+    (sequence, kv head) units up, three below) against the oracle."""
+    import torch
+    assert pasa.decode_splits(B, Skv, Hq, Hq // Hkv, D) == splits
+    w = W.custom(B, 1, Skv, Hq, Hkv, D, False, kind="bias", seed=B + Skv, bias=30.0)
+    q, k, v = W.generate(w)
+    tq, tk, tv = to_gpu(q, k, v)
+    say("decode default splits", (B, Skv, Hq, Hkv, D, splits))
+    o, lse = pasa.attn_decode(tq, tk, tv, scale=w.scale)
+    torch.cuda.synchronize()
+    ro, rl = attn_fp64(q, k, v, w.scale, False)
+    check_o(o.cpu().numpy(), ro, v, label=f"decode default splits {(B, Skv, Hq, Hkv, D)}")
+    assert lse_ok(lse.cpu().numpy(), rl[:, :, 0])
+
+
 def test_decode_combine_entry_on_oracle_partials(pasa):
     """pasa_attn_decode_combine fed with oracle partials over disjoint key
     ranges must reproduce the unsplit oracle (up to fp32/fp16 rounding)."""

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace pasa {
 
@@ -103,6 +104,31 @@ __device__ __forceinline__ void hexp2_pk4(h2* r) {
         "v_exp_f16_sdwa %3, %3 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
         "s_nop 1"
         : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]));
+}
+
+// hexp2_pk4 for two pairs, kept after the instruction that produced `after`.
+// The asm names `after` as an input and never reads it, so the compiler
+// cannot hoist the exponentials above that instruction; a scheduling fence
+// alone does not stop it.  One instruction separates the two writes to each
+// register, which is the one wait state that both hazards above ask for.
+__device__ __forceinline__ void hexp2_pk2_after(h2* r, const f16v& after) {
+    asm volatile("v_exp_f16_sdwa %0, %0 dst_sel:WORD_0 dst_unused:UNUSED_PRESERVE src0_sel:WORD_0\n\t"
+                 "v_exp_f16_sdwa %1, %1 dst_sel:WORD_0 dst_unused:UNUSED_PRESERVE src0_sel:WORD_0\n\t"
+                 "v_exp_f16_sdwa %0, %0 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
+                 "v_exp_f16_sdwa %1, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1\n\t"
+                 "s_nop 1"
+                 : "+v"(r[0]), "+v"(r[1])
+                 : "v"(after));
+}
+
+// f(std::integral_constant<int, i>{}) for i = B .. E-1, unrolled at compile
+// time, so that the body sees i as a constant expression.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 // fp16(c * a + z) for fp32 operands with one rounding (fused multiply-add in

@@ -458,50 +458,62 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 // compiler's own wait tracking.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); }
 
-// A operand of S^T = K Q^T: K row (row0 + sigma(n)), columns 16*kk + 8*hh..+7.
+// A operand of product kk of S^T = K Q^T for the 32-key sub-tile at row0:
+// K row (row0 + sigma(n)), columns 16*kk + 8*hh .. +7.
+template <int D>
+__device__ __forceinline__ h8 k_operand(const _Float16* Ks, int row0, int kk, int n, int hh) {
+    const int row = row0 + sigma(n);
+    return *(const h8*)(Ks + row * D + 8 * ((2 * kk + hh) ^ swz_k<D>(row)));
+}
+
 template <int D>
 __device__ __forceinline__ f16v qk_subtile_sw(const _Float16* Ks, int row0, const h8 (&qreg)[D / 16],
                                               int n, int hh) {
     f16v s = (f16v){};
-    const int row = row0 + sigma(n);
-    const _Float16* base = Ks + row * D;
-    const int sw = swz_k<D>(row);
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-        s = mfma_32x32x16(*(const h8*)(base + 8 * ((2 * kk + hh) ^ sw)), qreg[kk], s);
+    for (int kk = 0; kk < D / 16; ++kk) s = mfma_32x32x16(k_operand<D>(Ks, row0, kk, n, hh), qreg[kk], s);
     return s;
 }
 
-// O^T += V^T P^T for the 16-key chunks [ch0, ch0 + NCH) of a V tile.  The A
-// operand (head-dim row 32*dt + l%32, keys 16*ch + 8*hh + 0..7) is assembled
-// from two transposing LDS reads: in each 16-lane group, lane j receives
-// element (j % 4) of what lane 4*e + j/4 addressed, for e = 0..3; lane
-// 4*e + q addresses key (base + e), columns 4*q .. 4*q+3 of its group's 16.
-template <int D, int NCH>
-__device__ __forceinline__ void pv_chunks_tr(const _Float16* Vs, int ch0, const h2* P,
-                                             f16v (&acc)[D / 32], int lane) {
+// O^T += V^T P^T is taken per 16-key chunk ch of a V tile and 32-column
+// head-dim slice dt.  The A operand of that product (head-dim row
+// 32*dt + l%32, keys 16*ch + 8*hh + 0..7) is assembled from two transposing
+// LDS reads: in each 16-lane group, lane j receives element (j % 4) of what
+// lane 4*e + j/4 addressed, for e = 0..3; lane 4*e + q addresses key
+// (base + e), columns 4*q .. 4*q+3 of its group's 16.
+template <int D>
+__device__ __forceinline__ h8 v_operand_tr(const _Float16* Vs, int ch, int dt, int lane) {
     const int hh = lane >> 5;
     const int g2 = (lane >> 4) & 1;
     const int e = (lane >> 2) & 3;
     const int q = lane & 3;
+    const int rowa = 16 * ch + 8 * hh + e;   // keys +0..3
+    const int rowb = rowa + 4;               // keys +4..7
+    const int c = 4 * dt + 2 * g2 + (q >> 1);
+    const _Float16* pa = Vs + rowa * D + 8 * (c ^ swz_v<D>(rowa)) + 4 * (q & 1);
+    const _Float16* pb = Vs + rowb * D + 8 * (c ^ swz_v<D>(rowb)) + 4 * (q & 1);
+    const s4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)pa);
+    const s4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)pb);
+    const h4 ha = __builtin_bit_cast(h4, va), hb = __builtin_bit_cast(h4, vb);
+    return (h8){ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+}
+
+// B operand of chunk ch: the lane's 8 probabilities of that chunk's keys.
+__device__ __forceinline__ h8 p_operand(const h2* P, int ch) {
+    const h2 p0 = P[4 * ch + 0], p1 = P[4 * ch + 1], p2 = P[4 * ch + 2], p3 = P[4 * ch + 3];
+    return (h8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// O^T += V^T P^T for the chunks [ch0, ch0 + NCH) of a V tile.
+template <int D, int NCH>
+__device__ __forceinline__ void pv_chunks_tr(const _Float16* Vs, int ch0, const h2* P,
+                                             f16v (&acc)[D / 32], int lane) {
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-        const h2 p0 = P[4 * ch + 0], p1 = P[4 * ch + 1], p2 = P[4 * ch + 2], p3 = P[4 * ch + 3];
-        const h8 bp = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-        const int rowa = 16 * (ch0 + ch) + 8 * hh + e;   // keys +0..3
-        const int rowb = rowa + 4;                        // keys +4..7
-        const int swa = swz_v<D>(rowa), swb = swz_v<D>(rowb);
+        const h8 bp = p_operand(P, ch);
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-            const int c = 4 * dt + 2 * g2 + (q >> 1);
-            const _Float16* pa = Vs + rowa * D + 8 * (c ^ swa) + 4 * (q & 1);
-            const _Float16* pb = Vs + rowb * D + 8 * (c ^ swb) + 4 * (q & 1);
-            const s4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)pa);
-            const s4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)pb);
-            const h4 ha = __builtin_bit_cast(h4, va), hb = __builtin_bit_cast(h4, vb);
-            const h8 a = {ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
-            acc[dt] = mfma_32x32x16(a, bp, acc[dt]);
-        }
+        for (int dt = 0; dt < D / 32; ++dt)
+            acc[dt] = mfma_32x32x16(v_operand_tr<D>(Vs, ch0 + ch, dt, lane), bp, acc[dt]);
     }
 }
 

@@ -19,7 +19,10 @@ GPU): properties the sources rely on but the compiler could silently break.
 * every buffer load inside inline assembly (the LDS-DMA sequences) comes at
   least 5 wait states after a vector instruction that writes one of its
   scalar operands (v_readlane / v_readfirstlane and the like), for the same
-  reason.
+  reason,
+* the key-split head_dim-128 kernels keep their hand-placed matrix phase: four
+  exponentials after each of eight consecutive S^T products, not bunched in
+  front of them (the order the compiler chose on its own, 12 % slower).
 """
 import os
 import re
@@ -213,3 +216,26 @@ def test_inline_asm_buffer_loads_after_valu_sgpr_writes(asm, src):
                 break
     assert checked > 0
     assert not bad, bad[:5]
+
+
+def kernel_body(lines, name_re):
+    """Instructions of the one kernel whose symbol matches name_re."""
+    body, inside = None, False
+    for l in lines:
+        if not inside and l.endswith(":") and re.search(name_re, l):
+            inside, body = True, []
+            continue
+        if inside and l.startswith(".Lfunc_end"):
+            break
+        if inside and l and not l.startswith(".") and not l.endswith(":"):
+            body.append(l)
+    assert body, name_re
+    return body
+
+
+@pytest.mark.parametrize("var", [0, 1, 2], ids=["pasa", "strict", "naive"])
+def test_key_split_matrix_phase_keeps_exponentials_between_products(asm, var):
+    body = kernel_body(asm["pasa_fwd_d128.hip"], rf"fwd_kernelILi128ELb0ELi{var}ELb1E")
+    seq = "".join("M" if l.startswith("v_mfma") else "e" if l.startswith("v_exp_f16") else ""
+                  for l in body)
+    assert re.search(r"(Meeee){8}M", seq), seq[:200]

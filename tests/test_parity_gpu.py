@@ -469,6 +469,30 @@ def test_noncausal_full_round_vs_oracle(pasa, D):
     assert lse_ok(gl, rl)
 
 
+@pytest.mark.parametrize("variant", ["pasa", "strict", "naive"])
+def test_key_split_head_dim_128_vs_oracle(pasa, variant):
+    """The key-split kernel at head_dim 128, whose matrix phase is laid out in
+    slots by hand: a non-causal problem of few items (2 x 3 heads x 3 tiles of
+    128 rows) takes it.  1000 keys are 16 blocks of 64, eight per half, the
+    last one ragged (40 keys).  Checked against the oracle for each fp16
+    variant of the per-block rule; the naive kernel gets N(0, 1) inputs, whose
+    unscaled scores fp16 holds to a small fraction of a unit, and its own bar
+    (with a bias its raw head_dim-128 scores reach the thousands, where an
+    fp16 step is 1 or more)."""
+    naive = variant == "naive"
+    w = (W.custom(2, 300, 1000, 3, 1, 128, False, kind="normal", seed=91) if naive else
+         W.custom(2, 300, 1000, 3, 1, 128, False, kind="bias", seed=91, bias=25.0))
+    say("key split D128", variant, w)
+    (q, k, v), o, lse = run_fwd(pasa, w, naive=naive, strict=variant == "strict")
+    ro, rl = attn_fp64(q, k, v, w.scale, False)
+    assert nonfinite(o) == 0
+    if naive:
+        assert rel_rmse(o, ro) <= 5e-3
+    else:
+        check_o(o, ro, v, label=f"key split D128 {variant}")
+        assert lse_ok(lse, rl)
+
+
 # ----------------------------------------------------------------- streams, graphs
 def test_concurrent_streams_match_serial(pasa):
     """The library keeps no state: prefill and decode enqueued on two streams at

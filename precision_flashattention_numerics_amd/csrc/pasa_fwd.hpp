@@ -190,9 +190,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     _Float16* const Kst = smem + sg * tile_halves<D>();
     _Float16* const Vst = smem + (2 * kGroupStages + sg) * tile_halves<D>();
     // LDS DMA constants of this wave (the waves that share its tiles split the
-    // segments), and the stages' LDS byte addresses
-    constexpr int kLoadWaves = KS ? kWaves / 2 : kWaves;
-    const uint32_t w_u = __builtin_amdgcn_readfirstlane((uint32_t)(KS ? (w & 3) : w));
+    // segments), and the stages' LDS byte addresses.  At head_dim 128 without
+    // the key split only the group entering its vector phase issues a phase's
+    // loads, four segments per wave, so the group starting its products
+    // spends no time on them (c2 0.5-1.4 % faster; at head_dim 64 it was 4 %
+    // slower on a causal prefill).
+    constexpr bool kHalfLoad = !KS && D == 128;
+    constexpr int kLoadWaves = (KS || kHalfLoad) ? kWaves / 2 : kWaves;
+    const uint32_t w_u = __builtin_amdgcn_readfirstlane((uint32_t)((KS || kHalfLoad) ? (w & 3) : w));
     const TileDma<D, kBC, kLoadWaves, false, FP8> kdma(FP8 ? (uint32_t)kv_stride : stride_b, w_u, lane);
     const TileDma<D, kBC, kLoadWaves, true> vdma(stride_b, w_u, lane);
     constexpr uint32_t kTileBytes = tile_halves<D>() * 2;
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         vdma.issue(make_rsrc((const uint8_t*)vb + off, slab_bytes - off),
                    v_lds + (j & 1) * kTileBytes);
     };
-    if (nbl > 0) load_k(0);
+    if (nbl > 0 && (!kHalfLoad || grp == 0)) load_k(0);
 
     // ---- Q operand: lane holds Q[qi][16*kk + 8*hh .. +7]
     h8 qreg[FP8 ? 1 : KK];
@@ -253,18 +258,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __builtin_amdgcn_s_setprio(1);
         const bool pv = j >= 1 && active(j - 1);
         const bool qk = active(j);
-        if constexpr (KS && D == 128 && !FP8) {
+        if constexpr (D == 128 && !FP8) {
             if (pv && qk) {
-                // The same work in slots placed by hand: with the key split
-                // the kernel holds all 256 registers, and the compiler's own
-                // order kept only three K reads and one product of V reads
-                // ahead, with the exponentials bunched in front of the
-                // products (12 % slower).  Slot m issues the K read of product
-                // m + 4 and S^T product m; slots 0-7 add four exponentials of
-                // block j-1, ordered after the slot's product by naming its
-                // result; the V reads run four products ahead, from the last
-                // S^T slots on.  Products and exponentials are the same as
-                // below, in the same order per accumulator.
+                // The same work as below, in slots placed by hand.  The kernel
+                // holds all 256 registers, and with the key split the
+                // compiler's own order kept only three K reads and one product
+                // of V reads ahead, with the exponentials bunched in front of
+                // the products (12 % slower; without the key split the slots
+                // measure the same as its order).  Slot m issues the K read of
+                // product m + 4 and S^T product m; slots 0-7 add four
+                // exponentials of block j-1, ordered after the slot's product
+                // by naming its result; the V reads run four products ahead,
+                // from the last S^T slots on.  Products and exponentials are
+                // the same as below, in the same order per accumulator.
                 constexpr int NQ = NT * KK, NPV = 2 * NT * DT, AH = 4, AHV = 4;
                 h8 kop[AH + 1], vop[AHV + 1];
                 auto kread = [&](int m) { return k_operand<D>(Ks, 32 * (m / KK), m % KK, n, hh); };
@@ -374,10 +380,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // group 1 runs one phase behind.  K(m+1) is loaded from phase 2m and V(m)
     // from phase 2m+1 (spreading the loads' issue over both phases), into the
     // stages freed by K(m-1) and V(m-2); both have landed by the barrier that
-    // ends phase 2m+1, before either is read.
+    // ends phase 2m+1, before either is read (the waves that issued them wait
+    // for their loads before it).  With kHalfLoad the group in its matrix
+    // phase (group p % 2) issues none.
     const int nphase = nb0 > 0 ? 2 * nb0 + 2 : 0;   // nb0: the longer of the ranges
     for (int p = 0; p < nphase; ++p) {
-        if ((p & 1) == 0) {
+        if (kHalfLoad && grp == (p & 1)) {
+            // the other group issues this phase's loads
+        } else if ((p & 1) == 0) {
             const int m = p >> 1;
             if (m + 1 < nbl) load_k(m + 1);
         } else {

@@ -20,9 +20,10 @@ GPU): properties the sources rely on but the compiler could silently break.
   least 5 wait states after a vector instruction that writes one of its
   scalar operands (v_readlane / v_readfirstlane and the like), for the same
   reason,
-* the key-split head_dim-128 kernels keep their hand-placed matrix phase: four
+* the head_dim-128 fp16 kernels keep their hand-placed matrix phase: four
   exponentials after each of eight consecutive S^T products, not bunched in
-  front of them (the order the compiler chose on its own, 12 % slower).
+  front of them (the order the compiler chose on its own, 12 % slower with the
+  key split).
 """
 import os
 import re
@@ -233,9 +234,10 @@ def kernel_body(lines, name_re):
     return body
 
 
+@pytest.mark.parametrize("causal,ks", [(1, 0), (0, 0), (0, 1)], ids=["causal", "full", "key_split"])
 @pytest.mark.parametrize("var", [0, 1, 2], ids=["pasa", "strict", "naive"])
-def test_key_split_matrix_phase_keeps_exponentials_between_products(asm, var):
-    body = kernel_body(asm["pasa_fwd_d128.hip"], rf"fwd_kernelILi128ELb0ELi{var}ELb1E")
+def test_head_dim_128_matrix_phase_keeps_exponentials_between_products(asm, var, causal, ks):
+    body = kernel_body(asm["pasa_fwd_d128.hip"], rf"fwd_kernelILi128ELb{causal}ELi{var}ELb{ks}E")
     seq = "".join("M" if l.startswith("v_mfma") else "e" if l.startswith("v_exp_f16") else ""
                   for l in body)
     assert re.search(r"(Meeee){8}M", seq), seq[:200]

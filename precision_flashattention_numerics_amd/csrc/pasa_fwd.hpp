@@ -189,31 +189,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int sg = (KS && grp) ? 2 : 0;
     _Float16* const Kst = smem + sg * tile_halves<D>();
     _Float16* const Vst = smem + (2 * kGroupStages + sg) * tile_halves<D>();
-    // LDS DMA constants of this wave (the waves that share its tiles split the
-    // segments), and the stages' LDS byte addresses.  At head_dim 128 without
-    // the key split only the group entering its vector phase issues a phase's
-    // loads, four segments per wave, so the group starting its products
-    // spends no time on them (c2 0.5-1.4 % faster; at head_dim 64 it was 4 %
-    // slower on a causal prefill).
-    constexpr bool kHalfLoad = !KS && D == 128;
-    constexpr int kLoadWaves = (KS || kHalfLoad) ? kWaves / 2 : kWaves;
-    const uint32_t w_u = __builtin_amdgcn_readfirstlane((uint32_t)((KS || kHalfLoad) ? (w & 3) : w));
+    // LDS DMA constants of this wave, and the stages' LDS byte addresses.  A
+    // phase's loads are issued by four waves, four segments each (16 at
+    // head_dim 64), by the group that has the time for it (each choice
+    // measured against the others, outputs bitwise equal):
+    //  * head_dim 128 without the key split: the group entering its vector
+    //    phase, so the group starting its products spends nothing on them
+    //    (each wave runs both phases back to back; c2 0.5-1.4 % faster);
+    //  * head_dim 128 with the key split: each group its own tiles;
+    //  * head_dim 64: the group entering its matrix phase, which then waits
+    //    about 1000 cycles at the barrier for the vector phase; with the key
+    //    split it issues both groups' tiles (c3 1.9 %, a non-split causal
+    //    prefill 2.9 % faster than all eight waves issuing their own).
+    constexpr int kLoadWaves = kWaves / 2;
+    const uint32_t w_u = __builtin_amdgcn_readfirstlane((uint32_t)(w & 3));
     const TileDma<D, kBC, kLoadWaves, false, FP8> kdma(FP8 ? (uint32_t)kv_stride : stride_b, w_u, lane);
     const TileDma<D, kBC, kLoadWaves, true> vdma(stride_b, w_u, lane);
     constexpr uint32_t kTileBytes = tile_halves<D>() * 2;
     const uint32_t k_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)Kst);
     const uint32_t v_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)Vst);
     const uint32_t k_bytes = (uint32_t)(((int64_t)(Skv - 1) * kv_stride + D) * EB);
-    auto load_k = [&](int j) {   // local block j of this wave's range
-        const uint32_t off = (uint32_t)((blk0 + j) * kBC) * (uint32_t)(kv_stride * EB);   // < k_bytes
-        kdma.issue(make_rsrc(kb + off, k_bytes - off), k_lds + (j & 1) * kTileBytes);
+    // block b0 + j of the slab into stage j % 2 of the stage pair at klds / vlds
+    auto load_k_at = [&](int b0, uint32_t klds, int j) {
+        const uint32_t off = (uint32_t)((b0 + j) * kBC) * (uint32_t)(kv_stride * EB);   // < k_bytes
+        kdma.issue(make_rsrc(kb + off, k_bytes - off), klds + (j & 1) * kTileBytes);
     };
-    auto load_v = [&](int j) {
-        const uint32_t off = (uint32_t)((blk0 + j) * kBC) * stride_b;
-        vdma.issue(make_rsrc((const uint8_t*)vb + off, slab_bytes - off),
-                   v_lds + (j & 1) * kTileBytes);
+    auto load_v_at = [&](int b0, uint32_t vlds, int j) {
+        const uint32_t off = (uint32_t)((b0 + j) * kBC) * stride_b;
+        vdma.issue(make_rsrc((const uint8_t*)vb + off, slab_bytes - off), vlds + (j & 1) * kTileBytes);
     };
-    if (nbl > 0 && (!kHalfLoad || grp == 0)) load_k(0);
+    auto load_k = [&](int j) { load_k_at(blk0, k_lds, j); };   // local block j of this wave's range
+    auto load_v = [&](int j) { load_v_at(blk0, v_lds, j); };
+    // with the key split at head_dim 64: the other group's range and stages
+    constexpr bool kBothKS = KS && D == 64;
+    const int blk0_o = kBothKS ? __builtin_amdgcn_readfirstlane(grp ? 0 : nb0) : 0;
+    const int nbl_o = kBothKS ? __builtin_amdgcn_readfirstlane(grp ? nb0 : nblocks - nb0) : 0;
+    const uint32_t k_lds_o = kBothKS ? __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_void*)(smem + (grp ? 0 : 2) * tile_halves<D>())) : 0;
+    const uint32_t v_lds_o = kBothKS ? __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_void*)(smem + (2 * kGroupStages + (grp ? 0 : 2)) * tile_halves<D>())) : 0;
+    // block 0's K: with the key split each group its own, else group 0
+    if (nbl > 0 && (KS || grp == 0)) load_k(0);
 
     // ---- Q operand: lane holds Q[qi][16*kk + 8*hh .. +7]
     h8 qreg[FP8 ? 1 : KK];
@@ -381,18 +397,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // from phase 2m+1 (spreading the loads' issue over both phases), into the
     // stages freed by K(m-1) and V(m-2); both have landed by the barrier that
     // ends phase 2m+1, before either is read (the waves that issued them wait
-    // for their loads before it).  With kHalfLoad the group in its matrix
-    // phase (group p % 2) issues none.
+    // for their loads before it).  The group in its matrix phase is group
+    // p % 2; which group issues is chosen above.
     const int nphase = nb0 > 0 ? 2 * nb0 + 2 : 0;   // nb0: the longer of the ranges
     for (int p = 0; p < nphase; ++p) {
-        if (kHalfLoad && grp == (p & 1)) {
-            // the other group issues this phase's loads
-        } else if ((p & 1) == 0) {
+        const bool issuer = (KS && D == 128) || ((grp == (p & 1)) == (D == 64));
+        if (issuer) {
             const int m = p >> 1;
-            if (m + 1 < nbl) load_k(m + 1);
-        } else {
-            const int m = p >> 1;
-            if (m < nbl) load_v(m);
+            if ((p & 1) == 0) {
+                if (m + 1 < nbl) load_k(m + 1);
+                if (kBothKS && m + 1 < nbl_o) load_k_at(blk0_o, k_lds_o, m + 1);
+            } else {
+                if (m < nbl) load_v(m);
+                if (kBothKS && m < nbl_o) load_v_at(blk0_o, v_lds_o, m);
+            }
         }
         const int pp = p - grp;   // this group's own phase index
         if (pp >= 0) {

@@ -190,17 +190,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     _Float16* const Kst = smem + sg * tile_halves<D>();
     _Float16* const Vst = smem + (2 * kGroupStages + sg) * tile_halves<D>();
     // LDS DMA constants of this wave, and the stages' LDS byte addresses.  A
-    // phase's loads are issued by four waves, four segments each (16 at
-    // head_dim 64), by the group that has the time for it (each choice
-    // measured against the others, outputs bitwise equal):
-    //  * head_dim 128 without the key split: the group entering its vector
-    //    phase, so the group starting its products spends nothing on them
-    //    (each wave runs both phases back to back; c2 0.5-1.4 % faster);
-    //  * head_dim 128 with the key split: each group its own tiles;
+    // phase's loads (with the key split, both groups' tiles) are issued by the
+    // four waves of one group, by the group that has the time for it (each
+    // choice measured against all eight waves issuing their own share, outputs
+    // bitwise equal):
+    //  * head_dim 128: the group entering its vector phase, so the group
+    //    starting its products spends nothing on them (each wave runs both
+    //    phases back to back; c2 0.5-1.4 %, key-split shapes 3-5 % faster);
     //  * head_dim 64: the group entering its matrix phase, which then waits
-    //    about 1000 cycles at the barrier for the vector phase; with the key
-    //    split it issues both groups' tiles (c3 1.9 %, a non-split causal
-    //    prefill 2.9 % faster than all eight waves issuing their own).
+    //    about 1000 cycles at the barrier for the vector phase (c3 1.9 %, a
+    //    non-split causal prefill 2.9 % faster).
     constexpr int kLoadWaves = kWaves / 2;
     const uint32_t w_u = __builtin_amdgcn_readfirstlane((uint32_t)(w & 3));
     const TileDma<D, kBC, kLoadWaves, false, FP8> kdma(FP8 ? (uint32_t)kv_stride : stride_b, w_u, lane);
@@ -220,8 +219,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
     auto load_k = [&](int j) { load_k_at(blk0, k_lds, j); };   // local block j of this wave's range
     auto load_v = [&](int j) { load_v_at(blk0, v_lds, j); };
-    // with the key split at head_dim 64: the other group's range and stages
-    constexpr bool kBothKS = KS && D == 64;
+    // with the key split: the other group's range and stages
+    constexpr bool kBothKS = KS;
     const int blk0_o = kBothKS ? __builtin_amdgcn_readfirstlane(grp ? 0 : nb0) : 0;
     const int nbl_o = kBothKS ? __builtin_amdgcn_readfirstlane(grp ? nb0 : nblocks - nb0) : 0;
     const uint32_t k_lds_o = kBothKS ? __builtin_amdgcn_readfirstlane(
@@ -401,7 +400,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // p % 2; which group issues is chosen above.
     const int nphase = nb0 > 0 ? 2 * nb0 + 2 : 0;   // nb0: the longer of the ranges
     for (int p = 0; p < nphase; ++p) {
-        const bool issuer = (KS && D == 128) || ((grp == (p & 1)) == (D == 64));
+        const bool issuer = (grp == (p & 1)) == (D == 64);   // group p % 2 is in its matrix phase
         if (issuer) {
             const int m = p >> 1;
             if ((p & 1) == 0) {

@@ -225,6 +225,24 @@ int pasa_attn_decode_paged(const void* q, const void* k_pages, const void* v_pag
                            int num_splits, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* Whether the prefill entry points (pasa_attn_fwd and its strict, fp8 and naive
+ * variants) run a problem as key-split work items on num_cus compute units
+ * (host function, no device work; the entry points pass the current device's
+ * count, 256 on an MI355X).  A key-split item is 128 query rows whose two groups
+ * of waves take the two halves of the key range, merged in fp32 by the
+ * log-sum-exp rule ("Block Sparse Flash Attention" topic page, FoldAttention
+ * card: partials over disjoint key ranges compose).  The results differ from
+ * the 256-row items only by rounding.  Non-causal problems take it when the
+ * 256-row items would leave the last round of work items partly idle; causal
+ * problems when an estimate of the makespan of the items dealt longest first
+ * favours it by at least 5 % (short sequences or few heads, where the longest
+ * causal items set the time).
+ * Returns 1 (key split) or 0; PASA_ERR_INVALID for a size < 1, a causal flag
+ * other than 0 or 1, or num_cus outside [1, 65536]; PASA_ERR_UNSUPPORTED for a
+ * head_dim other than 64 or 128. */
+int pasa_attn_fwd_key_split(int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int head_dim,
+                            int causal, int num_cus);
+
 /* The split count pasa_attn_decode and pasa_attn_decode_paged use for
  * num_splits = 0 (host function, no device work): enough (sequence, key/value
  * head, split) work items for two waves per compute unit at head_dim 128; at

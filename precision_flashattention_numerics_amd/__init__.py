@@ -8,7 +8,7 @@ fails loudly if the library has not been built.
 
 _ENTRY = ("attn_fwd", "attn_fwd_strict", "attn_fwd_fp8", "naive_attn_fwd", "attn_decode",
           "attn_decode_noalloc", "attn_decode_paged", "attn_decode_combine",
-          "decode_splits", "decode_workspace_bytes", "decode_workspace", "status_string",
+          "decode_splits", "fwd_key_split", "decode_workspace_bytes", "decode_workspace", "status_string",
           "PasaError", "raw", "LIB_PATH")
 
 __all__ = list(_ENTRY)

@@ -43,6 +43,8 @@ _lib.pasa_attn_decode_paged.restype = _i
 _lib.pasa_attn_decode.restype = _i
 _lib.pasa_attn_decode_splits.argtypes = [_i, _i, _i, _i, _i]
 _lib.pasa_attn_decode_splits.restype = _i
+_lib.pasa_attn_fwd_key_split.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+_lib.pasa_attn_fwd_key_split.restype = _i
 _lib.pasa_attn_decode_workspace_bytes.argtypes = [_i, _i, _i, _i]
 _lib.pasa_attn_decode_workspace_bytes.restype = _sz
 _lib.pasa_attn_decode_combine.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]
@@ -176,6 +178,13 @@ def naive_attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, return
     """Naive fp16 Flash-Attention forward (overflow exhibit); same interface."""
     return _fwd(_lib.pasa_naive_attn_fwd, "pasa_naive_attn_fwd", q, k, v, causal, scale, out,
                 lse, return_lse, stream)
+
+
+def fwd_key_split(batch, seqlen_q, seqlen_kv, num_heads_q, head_dim, causal, num_cus=256) -> int:
+    """1 if the prefill runs this problem as key-split items on num_cus compute
+    units, 0 if not, a negative status for invalid arguments."""
+    return int(_lib.pasa_attn_fwd_key_split(batch, seqlen_q, seqlen_kv, num_heads_q, head_dim,
+                                            int(causal), num_cus))
 
 
 def decode_splits(batch, seqlen_kv, num_heads_q, gqa_group, head_dim) -> int:

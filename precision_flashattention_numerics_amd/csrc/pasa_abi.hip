@@ -110,6 +110,11 @@ int pasa_naive_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
                       gqa_group, head_dim, softmax_scale, causal, stream);
 }
 
+int pasa_attn_fwd_key_split(int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int head_dim,
+                            int causal, int num_cus) {
+    return V::fwd_key_split_query(batch, seqlen_q, seqlen_kv, num_heads_q, head_dim, causal, num_cus);
+}
+
 int pasa_attn_decode_splits(int batch, int seqlen_kv, int num_heads_q, int gqa_group,
                             int head_dim) {
     return V::decode_splits(batch, seqlen_kv, num_heads_q, gqa_group, head_dim);

@@ -48,6 +48,7 @@
 
 #include "kernels.hpp"
 #include "pasa_tile.hpp"
+#include "pasa_validate.hpp"
 
 namespace pasa {
 
@@ -108,13 +109,14 @@ __device__ __forceinline__ Item decode_item(int L, int N, int B, int Hq, int g, 
     return it;
 }
 
-// KS (key split, non-causal only): a workgroup takes 128 query rows, and its two
-// ping-pong groups hold the same rows and take the two halves of the key range,
-// each staging its own K/V tiles; the epilogue merges the two partial results
+// KS (key split): a workgroup takes 128 query rows, and its two ping-pong
+// groups hold the same rows and take the two halves of the key range, each
+// staging its own K/V tiles; the epilogue merges the two partial results
 // (running maximum, running sum, accumulator) in fp32 with the same
-// log-sum-exp rule as the decode's combine.  Twice the work items of half the
-// length each: for problems whose 256-row items leave a partly idle last round
-// of workgroups (e.g. 360 items on 256 CUs).
+// log-sum-exp rule as the decode's combine (a half in which a row sees no key
+// gets weight 0).  Twice the work items of half the length each: for problems
+// whose 256-row items leave a partly idle last round of workgroups (e.g. 360
+// items on 256 CUs), or whose longest causal items set the kernel's time.
 template <int D, bool CAUSAL, int VAR, bool KS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(
     const _Float16* __restrict__ q, const _Float16* __restrict__ k,
@@ -132,7 +134,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // takes the rest): at head_dim 64 the matrix phase has half the products
     // per score, so all of them go to the vector phase
     constexpr int EV = D == 64 ? 8 * NT : 0;
-    static_assert(!(KS && CAUSAL), "the key split is for non-causal attention");
     constexpr int kRows = KS ? kBR / 2 : kBR;   // query rows per workgroup
     constexpr int kGroupStages = KS ? 2 : 1;    // stage sets: one per group with KS
     __shared__ __attribute__((aligned(1024))) _Float16 smem[kGroupStages * fwd_smem_bytes<D>() / 2];
@@ -509,28 +510,43 @@ hipError_t launch_one(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// The key split pays when the 256-row items leave the last round of
-// workgroups partly idle: ceil(n128 / CUs) half-length rounds against
-// ceil(n256 / CUs) full ones (one workgroup per CU).
+// The item shape (pasa::validate::fwd_key_split) on this device's compute
+// units.  A causal choice simulates the dealing of up to 8 * CUs items, about
+// 20 us of host time, so each thread keeps the last shape's choice (and each
+// device's unit count): a repeated launch costs a comparison.
+struct SplitKey {
+    int dev, b, sq, skv, hq, d, causal;
+    bool operator==(const SplitKey& o) const {
+        return dev == o.dev && b == o.b && sq == o.sq && skv == o.skv && hq == o.hq && d == o.d &&
+               causal == o.causal;
+    }
+};
 bool use_key_split(const FwdArgs& a) {
-    if (a.causal) return false;
-    int dev = 0, n_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n_cu < 1)
-        return false;
-    const int64_t heads = (int64_t)a.batch * a.num_heads_q;
-    const int64_t n256 = heads * (((int64_t)a.seqlen_q + kBR - 1) / kBR);
-    const int64_t n128 = heads * (((int64_t)a.seqlen_q + kBR / 2 - 1) / (kBR / 2));
-    if (n128 > 0x7FFFFFFFLL) return false;
-    return (n128 + n_cu - 1) / n_cu < 2 * ((n256 + n_cu - 1) / n_cu);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    static thread_local SplitKey last = {-1, 0, 0, 0, 0, 0, 0};
+    static thread_local bool last_split = false;
+    const SplitKey key = {dev, a.batch, a.seqlen_q, a.seqlen_kv, a.num_heads_q, a.head_dim, a.causal};
+    if (key == last) return last_split;
+    static thread_local int cu_dev = -1, cu_count = 0;
+    if (dev != cu_dev) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+            return false;
+        cu_dev = dev;
+        cu_count = n;
+    }
+    last_split = validate::fwd_key_split(a.batch, a.seqlen_q, a.seqlen_kv, a.num_heads_q, a.head_dim,
+                                         a.causal, cu_count);
+    last = key;
+    return last_split;
 }
 
 template <int D, int VAR>
 hipError_t launch_causal_or_not(const FwdArgs& a, hipStream_t stream) {
-    if (a.causal) return launch_one<D, true, VAR, false>(a, stream);
-    if (use_key_split(a)) return launch_one<D, false, VAR, true>(a, stream);
-    return launch_one<D, false, VAR, false>(a, stream);
+    const bool ks = use_key_split(a);
+    if (a.causal) return ks ? launch_one<D, true, VAR, true>(a, stream) : launch_one<D, true, VAR, false>(a, stream);
+    return ks ? launch_one<D, false, VAR, true>(a, stream) : launch_one<D, false, VAR, false>(a, stream);
 }
 
 template <int D>

@@ -8,6 +8,11 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <functional>
+#include <queue>
+#include <vector>
+
 #include "../../include/pasa_attn.h"
 
 namespace pasa {
@@ -28,6 +33,76 @@ inline bool fits(int64_t a, int64_t b, int64_t c, int64_t d) {
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Causal prefill: time, in key-block intervals, of dealing the work items
+// longest first to n_cu compute units (one workgroup per unit).  An item of
+// `rows` query rows takes its key blocks (64 keys at head_dim 128, 128 at 64)
+// plus one interval of pipeline fill; with the key split its two halves run
+// side by side.  Every (batch, head) has the same items, and a later query
+// tile never sees fewer keys, so the tiles are dealt from the last one down.
+inline double causal_makespan(int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int head_dim,
+                              int rows, bool split, int n_cu) {
+    const int64_t kbc = head_dim == 64 ? 128 : 64;
+    const int64_t copies = (int64_t)batch * num_heads_q;
+    const int64_t shift = (int64_t)seqlen_kv - seqlen_q;
+    std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
+    for (int i = 0; i < n_cu; ++i) cu.push(0.0);
+    double end = 0.0;
+    for (int64_t t = ((int64_t)seqlen_q + rows - 1) / rows - 1; t >= 0; --t) {
+        const int64_t last = std::min<int64_t>((int64_t)seqlen_q - 1, t * rows + rows - 1);
+        const int64_t kv_end = std::max<int64_t>(0, std::min<int64_t>(seqlen_kv, last + shift + 1));
+        const int64_t nb = (kv_end + kbc - 1) / kbc;
+        const double len = (double)((split ? (nb + 1) / 2 : nb) + 1);
+        for (int64_t c = 0; c < copies; ++c) {
+            const double t0 = cu.top();
+            cu.pop();
+            cu.push(t0 + len);
+            end = std::max(end, t0 + len);
+        }
+    }
+    return end;
+}
+
+// Whether a prefill takes the key split (128-row items whose two ping-pong
+// groups take the two halves of the key range) on n_cu compute units.
+//  * Non-causal: when the 256-row items leave the last round of workgroups
+//    partly idle: ceil(n128 / CUs) half-length rounds against ceil(n256 / CUs)
+//    full ones.
+//  * Causal: when the estimate above for the split items, with an interval of
+//    the split kernel priced at 1.2 of one of the other (twice the tile loads,
+//    and every diagonal block in one half), is at least 5 % lower.  Calibrated
+//    on eight causal shapes (head_dim 64 and 128, 1024 to 32768 keys), where it
+//    picks the faster kernel every time.  Only problems of at most 8 * n_cu
+//    split items are considered: beyond that the items balance and the split
+//    loses.
+constexpr int kMaxCus = 65536;   // compute units the choice accepts (the simulation keeps one entry each)
+
+inline bool fwd_key_split(int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int head_dim,
+                          int causal, int n_cu) {
+    if (batch < 1 || seqlen_q < 1 || seqlen_kv < 1 || num_heads_q < 1 || n_cu < 1 || n_cu > kMaxCus ||
+        !supported_dim(head_dim))
+        return false;
+    const int64_t heads = (int64_t)batch * num_heads_q;
+    const int64_t n256 = heads * (((int64_t)seqlen_q + kFwdRows - 1) / kFwdRows);
+    const int64_t n128 = heads * (((int64_t)seqlen_q + kFwdRows / 2 - 1) / (kFwdRows / 2));
+    if (n128 > 0x7FFFFFFFLL) return false;
+    if (causal) {
+        if (n128 > 8 * (int64_t)n_cu) return false;
+        return 1.2 * causal_makespan(batch, seqlen_q, seqlen_kv, num_heads_q, head_dim, kFwdRows / 2, true, n_cu) <
+               0.95 * causal_makespan(batch, seqlen_q, seqlen_kv, num_heads_q, head_dim, kFwdRows, false, n_cu);
+    }
+    return (n128 + n_cu - 1) / n_cu < 2 * ((n256 + n_cu - 1) / n_cu);
+}
+
+// pasa_attn_fwd_key_split: 1 or 0, or the status for invalid arguments.
+inline int fwd_key_split_query(int batch, int seqlen_q, int seqlen_kv, int num_heads_q, int head_dim,
+                               int causal, int num_cus) {
+    if (batch < 1 || seqlen_q < 1 || seqlen_kv < 1 || num_heads_q < 1 || (causal != 0 && causal != 1) ||
+        num_cus < 1 || num_cus > kMaxCus)
+        return PASA_ERR_INVALID;
+    if (!supported_dim(head_dim)) return PASA_ERR_UNSUPPORTED;
+    return fwd_key_split(batch, seqlen_q, seqlen_kv, num_heads_q, head_dim, causal, num_cus) ? 1 : 0;
+}
 
 // Checks shared by the forward and decode entry points.
 inline int common(const void* q, const void* k, const void* v, const void* o, int batch,

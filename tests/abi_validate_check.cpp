@@ -67,6 +67,13 @@ int main() {
     EXPECT(V::decode_splits(64, 8192, 28, 7, 96) == 0);
     EXPECT(V::decode_splits(1, 1, 1, 1, 64) == 1);
     EXPECT(V::decode_splits(INT_MAX, INT_MAX, INT_MAX, 1, 128) >= 1);
+    EXPECT(V::fwd_key_split_query(1, 2048, 2048, 32, 128, 1, 256) == 1);
+    EXPECT(V::fwd_key_split_query(1, 4096, 4096, 28, 128, 1, 256) == 0);
+    EXPECT(V::fwd_key_split_query(2, 9216, 9216, 5, 64, 0, 256) == 1);
+    EXPECT(V::fwd_key_split_query(1, 64, 64, 1, 96, 0, 256) == PASA_ERR_UNSUPPORTED);
+    EXPECT(V::fwd_key_split_query(1, 64, 64, 1, 128, 0, 65537) == PASA_ERR_INVALID);
+    // the largest unit count: a causal problem of 8 * 65536 split items is simulated
+    EXPECT(V::fwd_key_split_query(1, 1 << 20, 1 << 20, 64, 64, 1, 65536) >= 0);
     EXPECT(V::workspace_bytes(0, 1, 1, 1) == 0);
     EXPECT(V::workspace_bytes(1, 1, 128, 1) == 512 + 256);
 
@@ -117,6 +124,12 @@ int main() {
                         calls += 5;
                     }
                 (void)V::decode_splits(a, b, c, 1, 128);
+                for (int cu : {1, 256})
+                    for (int causal : {0, 1}) {
+                        const int r = V::fwd_key_split_query(1, a, b, c > 0 ? c % 1024 + 1 : c, 128,
+                                                             causal, cu);
+                        EXPECT(r == 0 || r == 1 || r == PASA_ERR_INVALID);
+                    }
                 (void)V::workspace_bytes(a, b, 128, c);
                 (void)V::decode_workspace(A, (size_t)(unsigned)b, a, c, 64, 1);
                 calls += 3;

@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
                "pasa_attn_decode",
                "pasa_attn_decode_paged",
                "pasa_attn_decode_combine", "pasa_attn_decode_workspace_bytes",
-               "pasa_attn_decode_splits", "pasa_status_string"):
+               "pasa_attn_decode_splits", "pasa_attn_fwd_key_split", "pasa_status_string"):
         assert fn in names
 
 
@@ -69,6 +69,44 @@ def test_fwd_validation(lib, name):
     assert _fwd(lib, name, scale=float("nan")) == -2
     # more 256-row work items than an int counts (the tensors would not fit a GPU)
     assert _fwd(lib, name, B=65535, Sq=1, Skv=1, Hq=65535, g=65535) == -2
+
+
+# (batch, seqlen, heads, head_dim) of causal prefills timed both ways on one
+# MI355X (256 compute units), with the faster item shape: key split or not
+CAUSAL_SPLIT_MEASURED = [
+    ((1, 4096, 28, 128), 0),    # 148.4 vs 161.0 us with the split
+    ((2, 4096, 28, 128), 0),    # 242.3 vs 269.5
+    ((1, 8192, 28, 128), 0),    # 438.4 vs 480.2
+    ((1, 2048, 32, 128), 1),    # 63.6 vs 49.6
+    ((1, 1024, 16, 128), 1),    # 35.5 vs 24.0
+    ((1, 8192, 32, 64), 0),     # 326.0 vs 399.8
+    ((1, 16384, 6, 64), 0),     # 289.6 vs 305.3
+    ((1, 32768, 32, 128), 0),   # 7.53 vs 8.10 ms
+]
+
+
+@pytest.mark.parametrize("shape,split", CAUSAL_SPLIT_MEASURED, ids=lambda x: str(x))
+def test_fwd_key_split_picks_the_measured_faster_shape(lib, shape, split):
+    B, S, H, D = shape
+    assert lib.pasa_attn_fwd_key_split(B, S, S, H, D, 1, 256) == split
+
+
+def test_fwd_key_split_rules_and_errors(lib):
+    f = lib.pasa_attn_fwd_key_split
+    # non-causal: 360 items of 256 rows on 256 units (two rounds, the second
+    # partly idle) against 720 of 128 rows (three half-length rounds)
+    assert f(2, 9216, 9216, 5, 64, 0, 256) == 1
+    assert f(1, 1024, 1024, 64, 128, 0, 256) == 0    # exactly one full round
+    assert f(4, 2048, 2048, 32, 128, 0, 256) == 0
+    # causal, more than 8 * units split items: balanced, never split
+    assert f(8, 8192, 8192, 32, 128, 1, 256) == 0
+    # fewer units: the same problem has more items per unit
+    assert f(1, 2048, 2048, 32, 128, 1, 64) == 0
+    assert f(0, 64, 64, 1, 128, 0, 256) == -1
+    assert f(1, 64, 64, 1, 128, 2, 256) == -1
+    assert f(1, 64, 64, 1, 128, 0, 0) == -1
+    assert f(1, 64, 64, 1, 128, 0, 65537) == -1
+    assert f(1, 64, 64, 1, 96, 0, 256) == -2
 
 
 def test_decode_validation_and_sizes(lib):

@@ -493,6 +493,31 @@ def test_key_split_head_dim_128_vs_oracle(pasa, variant):
         assert lse_ok(lse, rl)
 
 
+@pytest.mark.parametrize("heads", [7, 700], ids=["key_split", "full_rows"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Sq,Skv", [(300, 300), (300, 1000), (500, 260)])
+def test_causal_item_shapes_vs_oracle(pasa, heads, D, Sq, Skv):
+    """Causal prefill through both item shapes: few heads take the key split
+    (two key halves merged in fp32), 700 heads exceed the split's item limit and
+    keep 256-row items.  Ragged tiles, bottom-right alignment with Sq < Skv, and
+    Sq > Skv, where the first rows see no key (O = 0, lse = -inf) and, with the
+    split, later rows see keys in only one half."""
+    split = pasa.fwd_key_split(1, Sq, Skv, heads, D, True)
+    assert split == (1 if heads == 7 else 0)
+    w = W.custom(1, Sq, Skv, heads, 1, D, True, kind="bias", seed=Sq + Skv + heads + D, bias=20.0)
+    say("causal item shape", "split" if split else "256 rows", w)
+    (q, k, v), o, lse = run_fwd(pasa, w)
+    ro, rl = attn_fp64(q, k, v, w.scale, True)
+    empty = np.isneginf(rl)
+    if empty.any():
+        b, h, i = np.nonzero(empty)
+        assert np.all(o[b, i, h] == 0)
+        assert np.all(np.isneginf(lse[empty]))
+    assert nonfinite(o) == 0
+    check_o(o, ro, v, label=f"causal {'split' if split else 'full'} D{D} {Sq}x{Skv}")
+    assert lse_ok(lse, rl)
+
+
 # ----------------------------------------------------------------- streams, graphs
 def test_concurrent_streams_match_serial(pasa):
     """The library keeps no state: prefill and decode enqueued on two streams at

@@ -15,8 +15,9 @@
  * Conventions shared by every entry point
  *  - Pointers are DEVICE pointers (HIP global memory) unless stated otherwise.
  *    The caller owns every buffer.  The library allocates nothing, never
- *    synchronises, keeps no global state and is safe to call from several host
- *    threads on different streams.
+ *    synchronises, keeps no global state (each host thread only remembers its
+ *    last prefill shape's item-shape choice) and is safe to call from several
+ *    host threads on different streams.
  *  - Work is enqueued on `stream` (0 = the null stream) and runs asynchronously;
  *    the return code reports argument validation and launch errors only.
  *  - Element types: q, k, v, o are IEEE binary16 (fp16); lse is fp32.

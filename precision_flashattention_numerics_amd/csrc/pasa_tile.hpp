@@ -121,10 +121,16 @@ __device__ __forceinline__ void fold_segment(RowState& st) {
 // is an fp16 addition.  This is usable while |c * score| stays well inside
 // the fp16 range (about 3.2e4): the rounding of R (ulp 16 there) moves the
 // largest P of a block up to 2^8 above 1.
-template <int NT, bool NAIVE, typename Vis, bool STRICT = false>
+// pre: work of the caller issued with the tile (the prefill's vector-phase
+// wave passes its phase's K/V loads); the compiler places it at the start of
+// the tile's code, ahead of the maxima.
+struct NoPre {
+    __device__ __forceinline__ void operator()() const {}
+};
+template <int NT, bool NAIVE, typename Vis, bool STRICT = false, typename Pre = NoPre>
 __device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 * NT],
                                                  RowState& st, float c, bool full, int cnt,
-                                                 Vis vis) {
+                                                 Vis vis, Pre pre = {}) {
     static_assert(!(STRICT && NAIVE), "the strict variant is a PASA variant");
     auto r16 = [](float x) { return STRICT ? (float)(_Float16)x : x; };
     _Float16 mb;
@@ -198,6 +204,7 @@ __device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 
         const float Rn = cnt > 0 ? fmaxf(st.R, top) : st.R;
         const _Float16 s = cnt > 0 ? (_Float16)(Rn - off) : (_Float16)0;
         const float noff = -(off + (float)s);
+        pre();
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -215,6 +222,7 @@ __device__ __forceinline__ _Float16 softmax_tile(const f16v (&S)[NT], h2 (&X)[8 
     } else {
         const _Float16 ch = (_Float16)c;
         h2 mm = (h2){kHalfNegInf, kHalfNegInf};
+        pre();
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll

@@ -410,7 +410,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     // p % 2; which group issues is chosen above.
     const int nphase = nb0 > 0 ? 2 * nb0 + 2 : 0;   // nb0: the longer of the ranges
     for (int p = 0; p < nphase; ++p) {
-        const bool issuer = (grp == (p & 1)) == (D == 64);   // group p % 2 is in its matrix phase
         auto dma = [&]() __attribute__((always_inline)) {
             const int m = p >> 1;
             if ((p & 1) == 0) {
@@ -422,13 +421,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
         };
         const int pp = p - grp;   // this group's own phase index
-        if (D == 128 && pp >= 0 && (pp & 1)) {
-            vphase(pp >> 1, dma);   // the issuing group: its loads go out with the tile
+        if constexpr (D == 128) {
+            if (pp >= 0 && (pp & 1)) vphase(pp >> 1, dma);   // the issuing group: its loads go out with the tile
+            else if (pp >= 0) mphase(pp >> 1);
+            else dma();   // group 1's first phase: nothing to compute, the loads to issue
         } else {
-            if (issuer) dma();
+            if (grp == (p & 1)) dma();   // group p % 2, in its matrix phase, issues
             if (pp >= 0) {
                 if ((pp & 1) == 0) mphase(pp >> 1);
-                else if constexpr (D != 128) vphase(pp >> 1, NoPre{});
+                else vphase(pp >> 1, NoPre{});
             }
         }
         // The barrier after an odd phase orders the LDS stages: the DMA into a

@@ -426,10 +426,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             else if (pp >= 0) mphase(pp >> 1);
             else dma();   // group 1's first phase: nothing to compute, the loads to issue
         } else {
-            if (grp == (p & 1)) dma();   // group p % 2, in its matrix phase, issues
-            if (pp >= 0) {
-                if ((pp & 1) == 0) mphase(pp >> 1);
-                else vphase(pp >> 1, NoPre{});
+            // head_dim 64: the vector-phase wave (the binding one) takes one
+            // test; the loads go out from group p % 2, in its matrix phase.
+            // In phase 0, group 1, still idle, issues the same loads as group
+            // 0 (identical bytes into the same stage, which nobody reads
+            // before the barrier that ends phase 1, where both have waited
+            // for their loads).  Keeping it out with one more test lays the
+            // loop out differently: 3-8 % slower against 5-6 % faster on the
+            // key-split shapes (same process, outputs bitwise equal).
+            if (pp >= 0 && (pp & 1)) {
+                vphase(pp >> 1, NoPre{});
+            } else {
+                dma();
+                if (pp >= 0) mphase(pp >> 1);
             }
         }
         // The barrier after an odd phase orders the LDS stages: the DMA into a

@@ -669,6 +669,24 @@ def main():
                               "nonfinite": nonfinite(o8.cpu().numpy())}
         del q8, k8, o8, l8
         torch.cuda.empty_cache()
+        # a short causal prefill of few work items (Qwen2-shaped heads, 2048
+        # tokens), where the longest causal items set the time: the library
+        # runs it as key-split items
+        ws_ = W.custom(1, 2048, 2048, 32, 8, 128, True, kind="bias", seed=12, bias=30.0)
+        tq, tk, tv = (torch.from_numpy(x).cuda() for x in W.generate(ws_))
+        os2, ls2 = pasa.attn_fwd(tq, tk, tv, causal=True, scale=ws_.scale)
+
+        def short():
+            pasa.attn_fwd(tq, tk, tv, causal=True, scale=ws_.scale, out=os2, lse=ls2)
+        warm(short, 0.1)
+        sh_ms, _ = timed_batches(short, 10, 5, stream)
+        n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+        other["causal_s2048_h32"] = {"ms": round(sh_ms, 5),
+                                     "tflops": round(ws_.flops() / (sh_ms * 1e-3) / 1e12, 2),
+                                     "key_split": pasa.fwd_key_split(1, 2048, 2048, 32, 128, True, n_cu),
+                                     "nonfinite": nonfinite(os2.cpu().numpy())}
+        del tq, tk, tv, os2, ls2
+        torch.cuda.empty_cache()
         out["other_configs"] = other
         log("peak microbenchmarks ...")
         peaks = measure_peaks(stream)

@@ -27,7 +27,9 @@ FLAGS = [
 #   * head_dim 128 keeps the default: iterative ILP scheduling was 0.7-1.7 %
 #     faster on the Qwen2-shaped prefill but 0.6-2.1 % slower on the
 #     long-context one (and spilled registers in the naive key-split kernel);
-#     minimum-register was 0.5 % slower on the Qwen2 shape;
+#     minimum-register was 0.5 % slower on the Qwen2 shape.  With the matrix
+#     phase laid out by hand both measured within 1.3 % of the default on five
+#     shapes;
 #   * the decode keeps the default (0.7 % slower with iterative ILP, 11 %
 #     slower with minimum-register).
 SOURCE_FLAGS = {

@@ -234,7 +234,8 @@ def kernel_body(lines, name_re):
     return body
 
 
-@pytest.mark.parametrize("causal,ks", [(1, 0), (0, 0), (0, 1)], ids=["causal", "full", "key_split"])
+@pytest.mark.parametrize("causal,ks", [(1, 0), (0, 0), (0, 1), (1, 1)],
+                         ids=["causal", "full", "key_split", "causal_key_split"])
 @pytest.mark.parametrize("var", [0, 1, 2], ids=["pasa", "strict", "naive"])
 def test_head_dim_128_matrix_phase_keeps_exponentials_between_products(asm, var, causal, ks):
     body = kernel_body(asm["pasa_fwd_d128.hip"], rf"fwd_kernelILi128ELb{causal}ELi{var}ELb{ks}E")
